@@ -1,0 +1,140 @@
+"""The attention forward pass, written out in float64 (test infrastructure only).
+
+What is computed (the readings are listed in DESIGN.md under "Readings"):
+
+  for every batch b and head h, with Q, K, V in R^{N x d}:
+    S   = scale * Q K^T                           (N x N, materialised)
+    S_ij = -inf for j > i                         (causal only; keys aligned with queries)
+    m_i = max_j S_ij
+    P_ij = exp(S_ij - m_i) / sum_j exp(S_ij - m_i)
+    O   = P V,   LSE_i = m_i + ln sum_j exp(S_ij - m_i)
+
+The pages describe the method only as a faster way to obtain *exactly* the
+result of standard attention (FlashAttention-2 wiki page, introduction and
+section "Leistung und Effizienz": identical results, exact and deterministic),
+whose quadratic cost comes from the full score matrix (same page, section
+"Hintergrund: Das Attention-Problem in Transformern").  So ``reference`` is
+that standard definition, not the tiled algorithm.  ``online`` follows the
+tiled algorithm's steps (running maximum, rescaling of the running sums,
+division by the row sum only after the last key tile; page "FlashAttention-
+Skalierung, Multi-GPU-Training und Gewichtsquantisierung", section 1, and the
+wiki page's section "Technische Architektur", item 1) and serves as an
+independent cross-check of the same result.  ``bruteforce`` is scalar Python
+with math.fsum for tiny inputs.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def _as_f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # torch tensor (bf16 is widened exactly through float32)
+        import torch
+
+        x = x.detach().to("cpu")
+        if x.dtype in (torch.bfloat16, torch.float16):
+            x = x.float()
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scores(q, k, scale, causal, rows):
+    """scale * q[rows] k^T with the causal mask applied (query index = row index)."""
+    s = scale * (q[rows] @ k.T)
+    if causal:
+        keys = np.arange(k.shape[0])
+        s[keys[None, :] > rows[:, None]] = -np.inf
+    return s
+
+
+def probabilities(q, k, causal: bool, scale: float, rows=None) -> np.ndarray:
+    """Softmax probabilities P for one head (q, k: [N, d]) -- rows of P sum to one."""
+    q, k = _as_f64(q), _as_f64(k)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    s = _scores(q, k, scale, causal, rows)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def reference(q, k, v, causal: bool, scale: float, rows=None):
+    """Plain definition of attention for [B, H, N, d] inputs.
+
+    Returns (O, LSE) as float64 arrays of shapes [B, H, R, d] and [B, H, R],
+    where R = N, or R = len(rows) when only the query rows ``rows`` are wanted
+    (every key is still used; this is how full-size outputs are sampled).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, d = q.shape
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((B, H, len(rows), v.shape[-1]))
+    lse = np.empty((B, H, len(rows)))
+    for b in range(B):
+        for h in range(H):
+            s = _scores(q[b, h], k[b, h], scale, causal, rows)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)
+            o[b, h] = (e / l) @ v[b, h]
+            lse[b, h] = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def online(q, k, v, causal: bool, scale: float, block: int = 64):
+    """The tiled, single-pass formulation over key blocks of ``block`` keys.
+
+    For each block of keys: new running max m' = max(m, rowmax S_blk); the
+    running sum and the unnormalised output are multiplied by exp(m - m')
+    before the block's exp(S_blk - m') terms are added; the division by the
+    row sum (and the logsumexp) happens once, after the last block.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, d = q.shape
+    o = np.empty(q.shape[:3] + (v.shape[-1],))
+    lse = np.empty((B, H, N))
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            m = np.full(N, -np.inf)
+            l = np.zeros(N)
+            acc = np.zeros((N, v.shape[-1]))
+            for j0 in range(0, N, block):
+                kk = k[b, h, j0:j0 + block]
+                s = scale * (q[b, h] @ kk.T)
+                if causal:
+                    keys = np.arange(j0, j0 + kk.shape[0])
+                    s[keys[None, :] > rows[:, None]] = -np.inf
+                m_new = np.maximum(m, s.max(axis=1))
+                # rows that have seen no visible key yet keep m = -inf and zero sums
+                alive = np.isfinite(m_new)
+                alpha = np.where(alive, np.exp(np.where(alive, m - m_new, 0.0)), 1.0)
+                p = np.where(alive[:, None], np.exp(s - np.where(alive, m_new, 0.0)[:, None]), 0.0)
+                l = alpha * l + p.sum(axis=1)
+                acc = alpha[:, None] * acc + p @ v[b, h, j0:j0 + block]
+                m = m_new
+            o[b, h] = acc / l[:, None]
+            lse[b, h] = m + np.log(l)
+    return o, lse
+
+
+def bruteforce(q, k, v, causal: bool, scale: float):
+    """Scalar triple loop with math.exp / math.fsum (tiny inputs only)."""
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, H, N, dv))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                visible = range(i + 1) if causal else range(N)
+                s = {j: scale * math.fsum(q[b, h, i, t] * k[b, h, j, t] for t in range(d)) for j in visible}
+                m = max(s.values())
+                w = {j: math.exp(s[j] - m) for j in visible}
+                z = math.fsum(w.values())
+                for c in range(dv):
+                    o[b, h, i, c] = math.fsum(w[j] * v[b, h, j, c] for j in visible) / z
+                lse[b, h, i] = m + math.log(z)
+    return o, lse

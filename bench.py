@@ -1,0 +1,204 @@
+"""Benchmark: attention forward TFLOP/s on one MI355X and fraction of dense MFMA peak.
+
+One step = one pass of the hot path over one batch of synthetic input:
+  * bf16 / fp32 workloads: one fa_fwd launch (query blocks x heads grid,
+    K/V tiles through LDS, online softmax, epilogue);
+  * the fp8 workload: three quantise+rotate launches (Q, K, V) and one
+    fa_fwd_fp8 launch.
+Inputs are resident in HBM before the timed region.  FLOPs counted:
+4*B*H*N^2*d, halved when causal (masking waste and exps are not counted).
+
+Prints exactly one JSON line on stdout; per-kernel details go to stderr.
+The default workload is bf16 causal B=4 H=16 N=2048 d=128.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synthetic  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # MI355X dense, AMD spec
+HBM_GBPS = 8000.0
+KERNEL_SOURCE = {"bf16": "attn_bf16.hip", "f32": "attn_f32.hip", "fp8": "attn_fp8.hip"}
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "exact_tiled_attention_18_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def hbm_traffic(workload: str, kernel_src: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when it is missing or the kernel changed since."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_source_sha") != source_sha(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def algorithmic_bytes(w) -> float:
+    """One read of Q, K, V and one write of O and LSE (fp8: codes + scales + bf16 O)."""
+    n = w.B * w.H * w.N * w.d
+    lse = 4 * w.B * w.H * w.N
+    if w.dtype == "f32":
+        return 4 * 4 * n + lse
+    if w.dtype == "bf16":
+        return 4 * 2 * n + lse
+    scales = 3 * 4 * w.B * w.H * ((w.N + 127) // 128)
+    return 3 * n + scales + 2 * n + lse
+
+
+def make_step(fa, w, dev):
+    q, k, v, signs = synthetic.workload_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    if w.dtype in ("f32", "bf16"):
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale, o=o, lse=lse)
+        return step, None
+    sg = torch.from_numpy(signs).to(dev)
+    nt = (w.N + 127) // 128
+    q8 = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    k8 = torch.empty_like(q8)
+    v8t = torch.empty((w.B, w.H, w.d, w.N), dtype=torch.uint8, device=dev)
+    qs, ks, vs = (torch.empty((w.B, w.H, nt), dtype=torch.float32, device=dev) for _ in range(3))
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def prepass():
+        fa.fa_quant_rotate_fp8(q, sg, False, x8=q8, x_scale=qs)
+        fa.fa_quant_rotate_fp8(k, sg, False, x8=k8, x_scale=ks)
+        fa.fa_quant_rotate_fp8(v, None, True, x8=v8t, x_scale=vs)
+
+    def attn():
+        fa.fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal=w.causal, scale=w.scale, o=o, lse=lse)
+
+    def step():
+        prepass()
+        attn()
+    return step, (prepass, attn)
+
+
+def time_loop(fn, iters: int) -> float:
+    """Seconds per call of fn, from HIP events on the stream the kernels run on."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / iters
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle, timed on this host on a bounded sample of the workload's heads."""
+    from oracle import attention as A
+
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = 1
+    q, k, v, _ = synthetic.workload_inputs(w)
+    heads = 0
+    t0 = time.perf_counter()
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        A.reference(q[sl], k[sl], v[sl], w.causal, w.scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops() * heads / (w.B * w.H)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of {w.name}, full N x N fp64 oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="bf16_causal_b4h16n2048d128",
+                    choices=[w.name for w in synthetic.WORKLOADS])
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards heads and "
+              "batches across GPUs with no exchange, so run it per GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import exact_tiled_attention_18_amd as fa
+
+    fa.load_library()
+    dev = "cuda:0"
+    w = synthetic.workload(args.workload)
+    step, parts = make_step(fa, w, dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    sec = time_loop(step, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tflops = w.flops() / sec / 1e12
+
+    # dominant kernel: the attention launch (for fp8, timed apart from the pre-pass)
+    if parts is None:
+        k_sec = sec
+    else:
+        prepass, attn = parts
+        pre_sec = time_loop(prepass, args.steps)
+        k_sec = time_loop(attn, args.steps)
+        pre_bytes = 3 * (2 + 1) * w.B * w.H * w.N * w.d + 3 * 4 * w.B * w.H * ((w.N + 127) // 128)
+        eprint(f"fp8 pre-pass: {pre_sec * 1e6:.1f} us for 3 tensors, {pre_bytes / pre_sec / 1e9:.0f} GB/s "
+               f"({pre_bytes / pre_sec / 1e9 / HBM_GBPS:.1%} of 8 TB/s)")
+    k_tflops = w.flops() / k_sec / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    eprint(f"{w.name}: step {sec * 1e6:.1f} us ({tflops:.1f} TFLOP/s); attention kernel {k_sec * 1e6:.1f} us "
+           f"= {k_tflops:.1f} TFLOP/s = {k_tflops / peak:.1%} of {peak} TFLOP/s; algorithmic HBM "
+           f"{algorithmic_bytes(w) / k_sec / 1e9:.0f} GB/s")
+
+    roofline = {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(k_tflops / peak, 4),
+                "traffic": hbm_traffic(w.name, KERNEL_SOURCE[w.dtype])}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
+    rec = {
+        "metric": "attention fwd TFLOP/s at 1 MI355X and % of dense MFMA peak (bf16, fp8)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": "1/sqrt(d)", "flops_per_step": w.flops()},
+        "frac_of_peak": round(tflops / peak, 4), "wall_s_timed": round(wall, 4),
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

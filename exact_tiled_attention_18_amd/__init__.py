@@ -1,0 +1,142 @@
+"""Exact tiled attention forward for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C-ABI library ``libfa.so`` (declared in
+``include/fa.h``).  The functions keep the C names and only marshal
+arguments: torch tensors supply device pointers, ``torch.cuda.current_stream()``
+supplies the stream, and output tensors are allocated here when the caller
+does not pass them.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback -- if the library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP = range(7)
+FA_F32, FA_BF16 = 0, 1
+TILE_ROWS = 128  # rows per fp8 quantisation tile
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"fa status {status}: {fa_status_string(status)}")
+
+
+def load_library():
+    """Load libfa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.fa_abi_version.restype = i32
+    lib.fa_abi_version.argtypes = []
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp]
+    lib.fa_quant_rotate_fp8.restype = i32
+    lib.fa_quant_rotate_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.fa_fwd_fp8.restype = i32
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, f32, vp]
+    _lib = lib
+    return lib
+
+
+def fa_abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FAError(status)
+
+
+def _check_dense(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None, stream=None):
+    """O, LSE = attention(q, k, v) for [B, H, N, d] float32 or bfloat16 tensors."""
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    dtype = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}.get(q.dtype, -1)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_dense(q, k, v, o, lse)
+    lib = load_library()
+    _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(causal),
+                      float(scale), dtype, _stream(stream)))
+    return o, lse
+
+
+def fa_quant_rotate_fp8(x, signs=None, transpose_out: bool = False, x8=None, x_scale=None, stream=None):
+    """e4m3 codes (uint8) and per-128-row-tile scales of x (bfloat16 [B, H, N, d])."""
+    B, H, N, d = x.shape
+    if x8 is None:
+        x8 = torch.empty((B, H, d, N) if transpose_out else (B, H, N, d), dtype=torch.uint8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((B, H, (N + TILE_ROWS - 1) // TILE_ROWS), dtype=torch.float32, device=x.device)
+    _check_dense(x, signs, x8, x_scale)
+    lib = load_library()
+    _check(lib.fa_quant_rotate_fp8(_ptr(x), _ptr(x8), _ptr(x_scale), _ptr(signs), B, H, N, d,
+                                   int(transpose_out), _stream(stream)))
+    return x8, x_scale
+
+
+def fa_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
+               o=None, lse=None, stream=None):
+    """O (bfloat16), LSE from e4m3 Q, K ([B, H, N, d]) and transposed V ([B, H, d, N])."""
+    B, H, N, d = q8.shape
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check_dense(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse)
+    lib = load_library()
+    _check(lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), 1,
+                          _ptr(o), _ptr(lse), B, H, N, d, int(causal), float(scale), _stream(stream)))
+    return o, lse
+
+
+def fp8_attention(q, k, v, signs, causal: bool = False, scale: float | None = None, stream=None):
+    """The FP8 path end to end: three pre-pass calls (Q and K rotated with the
+    same signs, V not rotated and written transposed) and the fp8 forward.
+    Returns (o, lse, (q8, k8, v8t, q_scale, k_scale, v_scale))."""
+    q8, qs = fa_quant_rotate_fp8(q, signs, False, stream=stream)
+    k8, ks = fa_quant_rotate_fp8(k, signs, False, stream=stream)
+    v8t, vs = fa_quant_rotate_fp8(v, None, True, stream=stream)
+    o, lse = fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale, stream=stream)
+    return o, lse, (q8, k8, v8t, qs, ks, vs)

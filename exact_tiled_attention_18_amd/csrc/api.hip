@@ -1,0 +1,124 @@
+// C-ABI entry points: argument validation, then one enqueue per kernel.
+// Validation never touches the GPU, so a rejected call has no side effect.
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "launch.h"
+
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+// Element count B*H*N*d without int64 overflow; also bounds the kernels'
+// 32-bit row indices and the size of a single launch.
+int shape_status(int64_t B, int64_t H, int64_t N, int64_t d, int64_t* count) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+  int64_t bh, bhn, n;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &n)) return FA_ERR_SHAPE;
+  if (N > INT32_MAX / 2) return FA_ERR_SHAPE;
+  // one launch: at most 2^24 workgroups of up to 256 threads
+  if (bh > 0 && (N + 63) / 64 > (int64_t(1) << 24) / bh) return FA_ERR_SHAPE;
+  *count = n;
+  return FA_OK;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)bbytes && y < x + (uintptr_t)abytes;
+}
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer";
+    case FA_ERR_SHAPE: return "invalid shape";
+    case FA_ERR_UNSUPPORTED: return "unsupported argument";
+    case FA_ERR_SCALE: return "non-finite scale";
+    case FA_ERR_ALIAS: return "output overlaps input";
+    case FA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+           int64_t N, int64_t d, int causal, float scale, int dtype, void* stream) {
+  int64_t n = 0;
+  if (int st = shape_status(B, H, N, d, &n)) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (n == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_UNSUPPORTED;
+  const int64_t tb = n * (dtype == FA_F32 ? 4 : 2), lb = B * H * N * 4;
+  for (const void* in : {q, k, v})
+    if (overlaps(o, tb, in, tb) || overlaps(lse, lb, in, tb)) return FA_ERR_ALIAS;
+  if (overlaps(o, tb, lse, lb)) return FA_ERR_ALIAS;
+
+  const fa::AttnArgs a{q, k, v, o, lse, B, H, N, d, causal, scale, static_cast<hipStream_t>(stream)};
+  return hip_status(dtype == FA_F32 ? fa::launch_attn_f32(a) : fa::launch_attn_bf16(a));
+}
+
+int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t* signs, int64_t B,
+                        int64_t H, int64_t N, int64_t d, int transpose_out, void* stream) {
+  int64_t n = 0;
+  if (int st = shape_status(B, H, N, d, &n)) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (transpose_out != 0 && transpose_out != 1) return FA_ERR_UNSUPPORTED;
+  if (n == 0) return FA_OK;
+  if (!x || !x8 || !x_scale) return FA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(x_scale, 4)) return FA_ERR_UNSUPPORTED;
+  const int64_t sb = B * H * ((N + 127) / 128) * 4;
+  if (overlaps(x8, n, x, 2 * n) || overlaps(x_scale, sb, x, 2 * n) || overlaps(x8, n, x_scale, sb))
+    return FA_ERR_ALIAS;
+  if (signs && (overlaps(x8, n, signs, d) || overlaps(x_scale, sb, signs, d))) return FA_ERR_ALIAS;
+
+  const fa::QuantArgs a{x, x8, x_scale, signs, B, H, N, d, transpose_out, static_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_quant_rotate_fp8(a));
+}
+
+int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+               const float* k_scale, const float* v_scale, int v_transposed, void* o, float* lse,
+               int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale, void* stream) {
+  int64_t n = 0;
+  if (int st = shape_status(B, H, N, d, &n)) return st;
+  if (d != 128 || v_transposed != 1) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (n == 0) return FA_OK;
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+      !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return FA_ERR_UNSUPPORTED;
+  const int64_t ob = 2 * n, lb = B * H * N * 4, sb = B * H * ((N + 127) / 128) * 4;
+  const void* ins[] = {q8, k8, v8};
+  const void* scs[] = {q_scale, k_scale, v_scale};
+  for (int i = 0; i < 3; ++i)
+    if (overlaps(o, ob, ins[i], n) || overlaps(lse, lb, ins[i], n) || overlaps(o, ob, scs[i], sb) ||
+        overlaps(lse, lb, scs[i], sb))
+      return FA_ERR_ALIAS;
+  if (overlaps(o, ob, lse, lb)) return FA_ERR_ALIAS;
+
+  const fa::Fp8AttnArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale,
+                          static_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_attn_fp8(a));
+}
+
+}  // extern "C"

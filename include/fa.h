@@ -1,0 +1,133 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention forward pass for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What is computed.  For every batch b and head h, with Q, K, V in R^{N x d}:
+ *     S = scale * Q K^T,  S_ij = -inf for j > i when causal,
+ *     O = softmax_rows(S) V,   LSE_i = ln sum_j exp(S_ij)   (natural log).
+ * The result is the one standard attention gives (FlashAttention-2 wiki page,
+ * introduction and section "Leistung und Effizienz": identical results, exact
+ * and deterministic); it is obtained without ever materialising S, by an
+ * outer loop over blocks of queries and an inner loop over tiles of keys and
+ * values that are staged in on-chip memory (same page, section "Hintergrund",
+ * and page "FlashAttention-Skalierung, Multi-GPU-Training und
+ * Gewichtsquantisierung", section 1), with the online softmax whose
+ * normalisation is applied once, after the last key tile (same section; wiki
+ * page, section "Technische Architektur", item 1).  The causal mask aligns
+ * queries and keys (query i sees keys 0..i); LSE is the logsumexp of the
+ * scaled, masked scores of each query row.
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers named as tensors are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees or keeps them.
+ *  - Tensors are contiguous and row-major: Q, K, V, O are [B, H, N, d];
+ *    LSE is float32 [B, H, N].
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work on it and return; they never synchronise.
+ *  - Arguments are validated before anything is enqueued; on any non-zero
+ *    status nothing was launched and no output was written.
+ *  - B, H or N equal to 0 is an empty problem: FA_OK, nothing is launched and
+ *    the tensor pointers are not inspected.
+ *  - Input values are not inspected; non-finite inputs propagate.
+ *  - Results are bitwise repeatable for the same inputs, shape and device
+ *    (no atomics, fixed reduction order).
+ *  - Calls are reentrant; the library holds no mutable state.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  FA_ERR_SHAPE = 2,       /* a negative size, or an element count beyond int64 */
+  FA_ERR_UNSUPPORTED = 3, /* head dim, dtype, flag or layout not provided      */
+  FA_ERR_SCALE = 4,       /* scale is NaN or infinite                          */
+  FA_ERR_ALIAS = 5,       /* an output overlaps an input                       */
+  FA_ERR_HIP = 6          /* the HIP runtime rejected a launch                 */
+};
+
+enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
+
+/* Version of this interface (FA_ABI_VERSION). */
+int fa_abi_version(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* fa_status_string(int status);
+
+/*
+ * fa_fwd -- attention forward in fp32 or bf16.
+ *   q, k, v : [B, H, N, d] of `dtype` (FA_F32: float32, FA_BF16: bfloat16).
+ *   o       : [B, H, N, d] of `dtype`, fully overwritten.
+ *   lse     : float32 [B, H, N], fully overwritten.
+ *   d       : 64 or 128.  N: any value >= 1 (no tile-size restriction).
+ *   causal  : 0 or 1.  scale: any finite value (0 gives uniform weights).
+ * Arithmetic: products and sums in fp32 (bf16 inputs multiply on bf16 MFMA
+ * with fp32 accumulation; the probabilities feeding the second product are
+ * rounded to bf16); O is rounded to `dtype` once, at the end.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, dtype, causal),
+ * FA_ERR_SCALE, FA_ERR_ALIAS (o or lse overlapping q, k or v, or each other),
+ * FA_ERR_HIP.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+           int dtype, void* stream);
+
+/*
+ * fa_quant_rotate_fp8 -- the FP8 pre-pass: block quantisation of one tensor,
+ * after an optional random orthogonal rotation (page "FlashAttention-
+ * Skalierung, Multi-GPU-Training und Gewichtsquantisierung", section 1, the
+ * FlashAttention-3 FP8 item: per-tile scales, and Q and K multiplied by random
+ * orthogonal matrices to spread outliers before quantisation).
+ *   x       : bfloat16 [B, H, N, d].
+ *   signs   : int8 [d] of +1/-1 (device), or NULL for no rotation (use NULL
+ *             for V).  With signs, each row x is replaced by x R with
+ *             R = diag(signs) H_d / sqrt(d), H_d the Sylvester-ordered
+ *             Hadamard matrix; Q and K must use the same signs.
+ *   x8      : OCP e4m3 codes (uint8).  transpose_out = 0: [B, H, N, d];
+ *             transpose_out = 1: [B, H, d, N] (the layout fa_fwd_fp8 wants for V).
+ *   x_scale : float32 [B, H, ceil(N/128)]: one scale per tile of 128 rows
+ *             (the last tile may be partial) = max |value| over the tile / 448,
+ *             or 1 for an all-zero tile.  code = e4m3(value / scale), rounded
+ *             to nearest even and saturated at +-448.
+ *   d       : 64 or 128.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, transpose_out),
+ * FA_ERR_ALIAS, FA_ERR_HIP.
+ */
+int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t* signs,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int transpose_out,
+                        void* stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward on e4m3 operands with per-tile scales.
+ *   q8, k8  : e4m3 codes [B, H, N, d] from fa_quant_rotate_fp8 with the same signs.
+ *   v8      : e4m3 codes of V (not rotated); v_transposed must be 1 and v8
+ *             laid out [B, H, d, N].
+ *   q_scale, k_scale, v_scale : float32 [B, H, ceil(N/128)] tile scales.
+ *   o       : bfloat16 [B, H, N, d];  lse: float32 [B, H, N].
+ *   d       : 128.  causal: 0 or 1.  scale: finite.
+ * Arithmetic: Q K^T and P V on fp8 MFMA with fp32 accumulation; the score of
+ * a (query tile, key tile) pair is multiplied by scale * q_scale * k_scale;
+ * probabilities are multiplied by 256 and rounded to e4m3 for the P V
+ * product (the factor is divided out with V's tile scale); the row sums use
+ * the unrounded fp32 probabilities.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, v_transposed,
+ * causal), FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP.
+ */
+int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+               const float* q_scale, const float* k_scale, const float* v_scale,
+               int v_transposed, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+               int64_t d, int causal, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

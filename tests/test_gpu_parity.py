@@ -1,0 +1,167 @@
+"""GPU parity: the HIP kernels (through the C-ABI) against the fp64 oracle.
+
+Small shapes are compared element by element over every output; the five
+full-size workloads are run in the exact launch configuration the benchmark
+times and compared on sampled heads and rows (which the oracle computes one
+by one, against all keys)."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import fp8 as F
+from tests import gpu_checks as G
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def fa():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import exact_tiled_attention_18_amd as fa
+    fa.load_library()
+    return fa
+
+
+def _run(fa, q, k, v, causal, scale):
+    o, lse = fa.fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# --------------------------------------------------------------------------- small shapes, every output
+SMALL = [(1, 2, n, d) for n in (1, 7, 64, 100, 128, 129, 255, 300, 513) for d in (64, 128)] + [(2, 3, 257, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}N{}d{}".format(*s))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_shapes(fa, dtype, shape, causal):
+    B, H, N, d = shape
+    G.log(f"case {dtype} {shape} causal={causal}")
+    q, k, v = synthetic.draw_qkv(B, H, N, d, seed=N * 7 + d + causal, dtype=dtype)
+    o, lse = _run(fa, q, k, v, causal, d ** -0.5)
+    assert o.dtype == q.dtype and lse.shape == (B, H, N)
+    eo, el = G.compare_attention(o, lse, q, k, v, causal, d ** -0.5, dtype)
+    tol_o, tol_l = G.TOL[dtype]
+    G.log(f"  max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+    assert eo <= tol_o and el <= tol_l
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.15, 0.5])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scale_edge_cases(fa, dtype, scale):
+    """scale 0 (uniform weights), a negative scale (max/min swap), a large one."""
+    G.log(f"case {dtype} scale={scale}")
+    q, k, v = synthetic.draw_qkv(1, 2, 300, 128, seed=99, dtype=dtype)
+    for causal in (False, True):
+        o, lse = _run(fa, q, k, v, causal, scale)
+        eo, el = G.compare_attention(o, lse, q, k, v, causal, scale, dtype)
+        G.log(f"  causal={causal} max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+        assert eo <= G.TOL[dtype][0] and el <= G.TOL[dtype][1]
+
+
+def test_empty_problem_launches_nothing(fa):
+    q = torch.empty((2, 3, 0, 64), dtype=torch.bfloat16, device=DEV)
+    o, lse = fa.fa_fwd(q, q, q)
+    assert o.shape == q.shape and lse.shape == (2, 3, 0)
+
+
+def test_unsupported_head_dim_raises(fa):
+    q = torch.zeros((1, 1, 16, 96), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd(q, q, q)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+
+
+# --------------------------------------------------------------------------- the five workloads at full size
+def _heads(B, H, n):
+    idx = np.linspace(0, B * H - 1, n).round().astype(int)
+    return [(int(i) // H, int(i) % H) for i in np.unique(idx)]
+
+
+@pytest.mark.parametrize("wi", [0, 1, 2, 3])
+def test_workload_full_size(fa, wi):
+    w = synthetic.WORKLOADS[wi]
+    G.log(f"case workload {w.name}")
+    q, k, v, _ = synthetic.workload_inputs(w)
+    o, lse = _run(fa, q, k, v, w.causal, w.scale)
+    tol_o, tol_l = G.TOL[w.dtype]
+    if w.N <= 2048:  # whole heads
+        eo, el = G.compare_attention(o, lse, q, k, v, w.causal, w.scale, w.dtype, heads=_heads(w.B, w.H, 6))
+        G.log(f"  whole heads: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+        assert eo <= tol_o and el <= tol_l
+    rows = G.sample_rows(w.N, 96, seed=wi)
+    eo, el = G.compare_attention(o, lse, q, k, v, w.causal, w.scale, w.dtype,
+                                 heads=_heads(w.B, w.H, 16 if w.N > 2048 else 64), rows=rows)
+    G.log(f"  sampled rows: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+    assert eo <= tol_o and el <= tol_l
+    # deterministic: a second launch reproduces every bit
+    o2, lse2 = _run(fa, q, k, v, w.causal, w.scale)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+# --------------------------------------------------------------------------- fp8
+def _fp8_case(fa, q, k, v, signs, causal, scale):
+    sg = None if signs is None else torch.from_numpy(signs).to(DEV)
+    o, lse, aux = fa.fp8_attention(q.to(DEV), k.to(DEV), v.to(DEV), sg, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse, aux
+
+
+@pytest.mark.parametrize("N", [1, 100, 128, 200, 256, 640])
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantizer_small(fa, N, d):
+    G.log(f"case quantizer N={N} d={d}")
+    q, _, _ = synthetic.draw_qkv(2, 2, N, d, seed=N + d, dtype="bf16", outlier_rate=0.01, outlier_scale=50.0)
+    signs = synthetic.draw_signs(d, N)
+    sg = torch.from_numpy(signs).to(DEV)
+    for rot in (True, False):
+        for tr in (False, True):
+            x8, xs = fa.fa_quant_rotate_fp8(q.to(DEV), sg if rot else None, tr)
+            torch.cuda.synchronize()
+            nb, nt = G.check_codes(x8, xs, q, signs if rot else None, transposed=tr)
+            G.log(f"  rotate={rot} transposed={tr}: {nb} of {nt} codes at rounding ties")
+            assert nb <= 1e-2 * nt
+
+
+@pytest.mark.parametrize("outliers", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 100, 128, 200, 256, 640])
+def test_fp8_small(fa, N, causal, outliers):
+    G.log(f"case fp8 N={N} causal={causal} outliers={outliers}")
+    d = 128
+    q, k, v = synthetic.draw_qkv(1, 2, N, d, seed=3 * N + causal, dtype="bf16",
+                                 outlier_rate=1e-3 if outliers else 0.0, outlier_scale=50.0)
+    signs = synthetic.draw_signs(d, N + 1)
+    o, lse, (q8, k8, v8t, qs, ks, vs) = _fp8_case(fa, q, k, v, signs, causal, d ** -0.5)
+    rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, causal, d ** -0.5, heads=[(0, 0), (0, 1)])
+    G.log(f"  vs dequantised oracle: scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
+    assert rel <= G.FP8_O_TOL and el <= G.FP8_LSE_TOL
+
+
+def test_fp8_workload_full_size(fa):
+    w = synthetic.WORKLOADS[4]
+    G.log(f"case workload {w.name}")
+    q, k, v, signs = synthetic.workload_inputs(w)
+    o, lse, (q8, k8, v8t, qs, ks, vs) = _fp8_case(fa, q, k, v, signs, w.causal, w.scale)
+    heads = _heads(w.B, w.H, 3)
+    # G5a: the pre-pass against the oracle quantiser on whole heads
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        for x, x8, xs, sg, tr in ((q, q8, qs, signs, False), (k, k8, ks, signs, False), (v, v8t, vs, None, True)):
+            nb, nt = G.check_codes(x8[sl], xs[sl], x[sl], sg, tr)
+            G.log(f"  head {(b, h)}: {nb} of {nt} codes at rounding ties")
+            assert nb <= 1e-2 * nt
+    # G5b: the attention kernel against the oracle of its dequantised operands
+    rows = G.sample_rows(w.N, 128, seed=4)
+    rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, w.causal, w.scale, heads=heads, rows=rows)
+    G.log(f"  vs dequantised oracle: scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
+    assert rel <= G.FP8_O_TOL and el <= G.FP8_LSE_TOL
+    # reported, not gated: error against the un-quantised inputs (exact oracle)
+    eo, elx = G.compare_attention(o, lse, q, k, v, w.causal, w.scale, "bf16", heads=heads[:1], rows=rows)
+    G.log(f"  vs un-quantised oracle (report only): max|dO| {eo:.3e}  max|dLSE| {elx:.3e}")
+    o2, lse2, _ = _fp8_case(fa, q, k, v, signs, w.causal, w.scale)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)

@@ -13,6 +13,7 @@ LIB = os.path.join(PKG, "libfa.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["api.hip", "attn_f32.hip", "attn_bf16.hip", "quant_fp8.hip", "attn_fp8.hip"]
+EXTRA = {}  # per-source extra flags
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -26,7 +27,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -7,27 +7,58 @@
 //     batch), so a single head is spread over many compute units;
 //   * inner loop over key/value tiles staged through LDS;
 //   * online softmax: running row maximum, exp2 of the shifted scores,
-//     correction of the running sum and the unnormalised output by
-//     exp2(m_old - m_new), and a single division by the row sum after the
-//     last tile;
-//   * every wavefront owns whole query rows, so row maxima and sums never
-//     go through LDS.
+//     correction of the running sums and of the unnormalised output, and a
+//     single division by the row sum after the last tile;
+//   * every wavefront owns whole query rows, so row maxima and sums never go
+//     through LDS.
+// The overlap of the matrix products with the softmax and with data movement
+// follows the FlashAttention-3 ideas (same page, section 1; news page on
+// FlashAttention-3, section "Innovationen"), rebuilt for CDNA4 below.
 //
-// MI355X mapping.  A wavefront owns 32*QB queries.  Scores are computed
-// transposed, S^T = K Q^T, with K as the MFMA A operand (from LDS) and Q as
-// the B operand (registers, loaded once).  In the 32x32 accumulator layout a
-// lane then holds one query column (lane % 32) and 16 of the 32 keys of the
-// block, so the row statistics of a query live in one lane plus its partner
-// 32 lanes away: the row max needs one cross-half exchange per tile and the
-// row sum is kept per lane until the epilogue.  The K rows fed to the A
-// operand are permuted (bits 2 and 3 of the row index swapped) so that a
-// lane's 16 keys come out as two runs of 8 consecutive keys, which is exactly
-// the operand layout the second product O^T += V^T P^T needs for P^T as its
-// B operand: the probabilities go from accumulator registers to operand
-// registers with one bf16 conversion and no data movement.  O^T is kept in
-// the same column-per-query layout, so the per-tile correction factor is a
-// lane-local multiply.  V is transposed into LDS on its way in (keys
-// contiguous) for the A operand of the second product.
+// Wavefront layout.  A wavefront owns 64 queries (two blocks of 32).  Scores
+// are computed transposed, S^T = K Q^T, with K as the MFMA A operand (from
+// LDS) and Q as the B operand (registers, loaded once).  In the 32x32
+// accumulator layout a lane then holds one query (lane % 32) and 16 of the 32
+// keys of a tile, so a query's statistics live in one lane plus its partner
+// 32 lanes away.  The K rows fed to the A operand are permuted (bits 2 and 3
+// of the row index swapped) so that a lane's 16 keys come out as two runs of
+// 8 consecutive keys: exactly the B-operand layout of P^T in the second
+// product O^T += V^T P^T, so the probabilities go from accumulators to
+// operand registers with one bf16 conversion.  O^T keeps the query-per-lane
+// layout, so rescaling it is lane-local.  V stays row-major in LDS; its
+// transposed A operand comes from the transposing read ds_read_b64_tr_b16.
+// Owning 64 queries per wavefront halves the LDS bytes read per MFMA compared
+// with 32, which keeps LDS bandwidth below the matrix-core rate.
+//
+// Software pipeline.  One wavefront per SIMD, so each has the whole 512-entry
+// register file: Q fragments and O accumulators sit in AGPRs (only MFMAs read
+// them), scores, probabilities and staging in VGPRs.  Step t (one 32-key
+// tile) issues the 16 MFMAs of S_{t+1} = K_{t+1} Q^T, the 16 MFMAs of
+// O^T += V_{t-1}^T P_{t-1}^T and the vector work of the softmax of S_t.  None
+// depends on another, so the step is cut into D/16 chunks, each holding 2 + 2
+// MFMAs, one slice of the softmax and the LDS reads of the next chunk's
+// operands; scheduling barriers keep that order, so the matrix core runs
+// while the vector unit computes exponentials, and LDS latency is hidden one
+// chunk ahead -- the interleaving of matmul and softmax the pages describe
+// for Hopper, inside one wavefront.  Every step issues the same instructions
+// (no data-dependent branches): at t = 0 the P V product multiplies zero
+// probabilities with a zeroed V slot, and past the last tile the scores of a
+// stale K slot are computed and never used.  K/V tiles go HBM -> registers one
+// step ahead and registers -> LDS into three rotating slots per operand
+// (written two steps before use), so one workgroup barrier per step suffices
+// although the next step's first operands are read before it.
+//
+// Lazy rescaling.  The softmax shift m of a row only moves when the row
+// maximum exceeds it by more than 8 (log2 units); otherwise probabilities are
+// exp2(c*s - m) <= 2^8 and the running sums and output keep their scale.  The
+// shift cancels in O = acc / l and is added back in LSE = m + log2(l), so the
+// result is unchanged while the rescale of O runs on only a few tiles; it is
+// applied at the end of the step, after the step's products are issued.
+//
+// Two row sums.  l sums the fp32 probabilities and gives LSE; lh sums the
+// bf16-rounded probabilities that actually enter P V (v_dot2_f32_bf16 against
+// (1, 1)) and normalises O, which makes O an exact weighted mean of V under
+// the rounded weights.
 #include "fa_device.h"
 #include "launch.h"
 
@@ -35,231 +66,456 @@ namespace fa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kBc = 64;  // keys per tile
+constexpr int kQB = 2;            // 32-query blocks per wavefront
+constexpr int kW = 32 * kQB;      // queries per wavefront
+constexpr int kBr = kWaves * kW;  // queries per workgroup
+constexpr int kBc = 32;           // keys per tile
+constexpr int kSlots = 3;         // LDS slots per operand
+constexpr int kThreads = kWaves * 64;
+constexpr float kRescaleSlack = 8.f;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 template <int D>
-struct Smem {
-  static constexpr int KS = D + 8;    // K tile row stride (bf16 elements), 16-byte aligned rows
-  static constexpr int VS = kBc + 8;  // V^T tile row stride
-  uint16_t k[kBc * KS];
-  uint16_t vt[D * VS];
+struct Layout {
+  static constexpr int KS = D * 2 + 16;  // K row stride (bytes): conflict-free 16-byte row reads
+  static constexpr int VS = D * 2 + 64;  // V row stride (bytes): conflict-free transposing reads
+  static constexpr int KSLOT = kBc * KS;
+  static constexpr int VSLOT = kBc * VS;
+  static constexpr int BYTES = kSlots * (KSLOT + VSLOT);
+  static constexpr int CHUNKS = kBc * D * 2 / 16 / kThreads;  // 16-byte copies per thread per operand tile
 };
 
-__device__ __forceinline__ int permuted_row(int i) {  // swap bits 2 and 3
-  return i ^ ((((i >> 2) ^ (i >> 3)) & 1) * 0xC);
+__device__ __forceinline__ int permuted_row(int i) { return i ^ ((((i >> 2) ^ (i >> 3)) & 1) * 0xC); }
+
+// 4 bf16 of V^T: lane l of each 16-lane group receives V[K0 + j][D0 + l], j = 0..3,
+// when lane k of the group points at V[K0 + k/4][D0 + 4*(k%4)].
+__device__ __forceinline__ v4i16 tr_read(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
-// key offset (within a 32-key block) of accumulator register r in lane half g
-__device__ __forceinline__ int key_of_reg(int r, int g) { return (r & 7) + g * 8 + (r & 8) * 2; }
 
-template <int D, bool CAUSAL, int QB>
-__global__ __launch_bounds__(kWaves * 64) void attn_fwd_bf16_kernel(
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D, bool CAUSAL>
+struct Attn {
+  using Ly = Layout<D>;
+  static constexpr int DK = D / 16;  // k-steps of S = chunks per step
+  static constexpr int DB = D / 32;  // 32-row blocks of O^T
+  static constexpr int NCH = DK;     // chunks per step; PV chunk ch is (db, mm) = (ch % DB, ch / DB)
+  static_assert(DB * 2 == NCH, "one PV operand per chunk");
+
+  // ---- per-thread state
+  bf16x8 qf[kQB][DK];
+  f32x16 oacc[DB][kQB];
+  f32x16 sbuf[2][kQB];     // S^T of two consecutive tiles
+  bf16x8 pbuf[2][kQB][2];  // P^T (bf16) of two consecutive tiles
+  bf16x8 kop[2], vop[2];   // operand prefetch, by chunk parity
+  uint4 stg_k[Ly::CHUNKS], stg_v[Ly::CHUNKS];
+  float m[kQB], l[kQB], lh[kQB], alpha[kQB], msub[kQB], mx[kQB], rs[kQB];
+
+  // ---- per-workgroup constants
+  const uint16_t* kg;
+  const uint16_t* vg;
+  char* kslot;
+  char* vslot;
+  size_t base;
+  int N, qw0, lane, g, li, tid;
+  float c;  // > 0: scale * log2(e) in magnitude
+
+  // Register-class hints (empty asm, no instructions): Q fragments and the O
+  // accumulators live in AGPRs -- only MFMAs read them -- leaving the
+  // architectural VGPRs to the scores, probabilities and staging that the
+  // vector unit works on.
+  __device__ __forceinline__ void pin_agprs() {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(oacc[db][qb]));
+    }
+  }
+
+  __device__ __forceinline__ bf16x8 read_k(int slot, int ks) const {
+    return *reinterpret_cast<const bf16x8*>(kslot + slot * Ly::KSLOT + permuted_row(li) * Ly::KS + g * 16 +
+                                            ks * 32);
+  }
+  __device__ __forceinline__ bf16x8 read_v(int slot, int ch) const {
+    const int db = ch % DB, mm = ch / DB;
+    const int grp16 = lane >> 4, l16 = lane & 15;
+    const char* pa = vslot + slot * Ly::VSLOT + (mm * 16 + 8 * (grp16 >> 1) + (l16 >> 2)) * Ly::VS +
+                     (db * 32 + 16 * (grp16 & 1) + 4 * (l16 & 3)) * 2;
+    const v4i16 lo = tr_read(pa), hi = tr_read(pa + 4 * Ly::VS);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // thread index as an opaque value: the copy addresses derived from it are
+  // recomputed in every step (a few integer ops) instead of being hoisted out of
+  // the tile loop, where they would occupy registers across the whole loop
+  __device__ __forceinline__ int fresh_tid() const {
+    int x = tid;
+    asm volatile("" : "+v"(x));
+    return x;
+  }
+  // piece i of a tile copy covers row  tid / (D/8) + i * (kThreads / (D/8)),  column  8 * (tid % (D/8))
+
+  // ---- HBM -> registers -> LDS copies of one operand tile (16-byte pieces, coalesced rows)
+  template <bool GUARD>
+  __device__ __forceinline__ void load_tile(const uint16_t* src, int t, uint4 (&stg)[Ly::CHUNKS]) const {
+    const int ft = fresh_tid();
+    const int row0 = ft / (D / 8), col = (ft % (D / 8)) * 8;
+#pragma unroll
+    for (int i = 0; i < Ly::CHUNKS; ++i) {
+      const int row = row0 + i * (kThreads / (D / 8));
+      const int key = t * kBc + row;
+      if (!GUARD) {
+        stg[i] = *reinterpret_cast<const uint4*>(src + base + (size_t)key * D + col);
+      } else {
+        // rows past N: read a valid row and replace it by zeros (no branch)
+        const uint4 x = *reinterpret_cast<const uint4*>(src + base + (size_t)min(key, N - 1) * D + col);
+        const bool in = key < N;
+        stg[i] = make_uint4(in ? x.x : 0u, in ? x.y : 0u, in ? x.z : 0u, in ? x.w : 0u);
+      }
+    }
+  }
+  __device__ __forceinline__ void store_tile(char* dst, int stride, const uint4 (&stg)[Ly::CHUNKS]) const {
+    const int ft = fresh_tid();
+    char* p = dst + (ft / (D / 8)) * stride + (ft % (D / 8)) * 16;
+#pragma unroll
+    for (int i = 0; i < Ly::CHUNKS; ++i)
+      *reinterpret_cast<uint4*>(p + i * (kThreads / (D / 8)) * stride) = stg[i];
+  }
+
+  // ---- softmax of the scores in sbuf[B] (tile t) -> pbuf[B].  The launcher
+  // guarantees c > 0 (a negative scale negates Q, a zero scale zeroes Q), so
+  // the row maximum of c*s is c*max(s) and -inf marks a masked score.
+  __device__ __forceinline__ void mask_scores(int B, int t) {
+    // register r of lane half g holds key t*kBc + (r & 7) + 8*g + 2*(r & 8),
+    // visible to query qi iff that key <= min(qi, N - 1)
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int qi = qw0 + qb * 32 + li;
+      const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - t * kBc - g * 8;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((r & 7) + (r & 8) * 2 > lim) sbuf[B][qb][r] = -kInf;
+    }
+  }
+  __device__ __forceinline__ void row_max(int B, int qb) {
+    float a = sbuf[B][qb][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) a = fmaxf(a, sbuf[B][qb][r]);
+    mx[qb] = a;
+  }
+  __device__ __forceinline__ void new_shift(int qb) {
+    const float mt = c * fmaxf(mx[qb], xor32(mx[qb]));  // -inf when no key of the tile is visible
+    const float m_new = mt > m[qb] + kRescaleSlack ? mt : m[qb];
+    // 0 when m was -inf, exactly 1 when unchanged (also for rows with no visible key yet)
+    alpha[qb] = m_new == -kInf ? 1.f : exp2_fast(m[qb] - m_new);
+    m[qb] = m_new;
+    l[qb] *= alpha[qb];
+    lh[qb] *= alpha[qb];
+    msub[qb] = m_new == -kInf ? 0.f : m_new;
+    rs[qb] = 0.f;
+  }
+  __device__ __forceinline__ void exps(int B, int e0, int e1) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) {
+      const int qb = e / 16, r = e % 16;
+      const float p = exp2_fast(fmaf(sbuf[B][qb][r], c, -msub[qb]));  // masked: exp2(-inf) = 0
+      sbuf[B][qb][r] = p;
+      rs[qb] += p;
+    }
+  }
+  __device__ __forceinline__ void pack(int B, int qb) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float h_acc = lh[qb];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 wv;
+      wv.x = pack_bf16x2(sbuf[B][qb][8 * h + 0], sbuf[B][qb][8 * h + 1]);
+      wv.y = pack_bf16x2(sbuf[B][qb][8 * h + 2], sbuf[B][qb][8 * h + 3]);
+      wv.z = pack_bf16x2(sbuf[B][qb][8 * h + 4], sbuf[B][qb][8 * h + 5]);
+      wv.w = pack_bf16x2(sbuf[B][qb][8 * h + 6], sbuf[B][qb][8 * h + 7]);
+      pbuf[B][qb][h] = __builtin_bit_cast(bf16x8, wv);
+      h_acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), ones, h_acc, false);
+      h_acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), ones, h_acc, false);
+      h_acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), ones, h_acc, false);
+      h_acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), ones, h_acc, false);
+    }
+    lh[qb] = h_acc;
+    l[qb] += rs[qb];
+  }
+  // slice ch of the softmax work (mask, row max, shift, 32 exponentials, packing)
+  template <bool GUARD>
+  __device__ __forceinline__ void softmax_slice(int ch, int B, int t) {
+    if (NCH == 8) {
+      switch (ch) {
+        case 0:
+          if (GUARD) mask_scores(B, t);
+          row_max(B, 0);
+          row_max(B, 1);
+          break;
+        case 1: new_shift(0); new_shift(1); break;
+        case 2: exps(B, 0, 7); break;
+        case 3: exps(B, 7, 14); break;
+        case 4: exps(B, 14, 21); break;
+        case 5: exps(B, 21, 28); break;
+        case 6: exps(B, 28, 32); pack(B, 0); break;
+        default: pack(B, 1); break;
+      }
+    } else {
+      switch (ch) {
+        case 0:
+          if (GUARD) mask_scores(B, t);
+          row_max(B, 0);
+          row_max(B, 1);
+          new_shift(0);
+          new_shift(1);
+          break;
+        case 1: exps(B, 0, 16); break;
+        case 2: exps(B, 16, 32); pack(B, 0); break;
+        default: pack(B, 1); break;
+      }
+    }
+  }
+
+  template <int B>
+  __device__ __forceinline__ void last_pv(int slot) {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const bf16x8 a = ch == 0 ? vop[0] : read_v(slot, ch);
+      const int db = ch % DB, mm = ch / DB;
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) oacc[db][qb] = mfma(a, pbuf[B][qb][mm], oacc[db][qb]);
+    }
+  }
+
+  // ---- one pipeline step for tile t: S_{t+1} into sbuf[B^1], O += P_{t-1} V_{t-1},
+  // softmax of sbuf[B] -> pbuf[B]; LDS writes of K_{t+3}, V_{t+1}; loads of K_{t+4}, V_{t+2}.
+  // GUARD steps (the first, the causal diagonal and the tail) mask scores and bound
+  // the tile loads; the others (1 <= t, tiles t, t+1 unmasked, tile t + 4 inside N)
+  // need neither.
+  template <bool GUARD, int B>
+  __device__ __forceinline__ void step(int t, int sk_next, int sk_w, int sv_pv, int sv_next, int sv_w) {
+    f32x16 (&snext)[kQB] = sbuf[B ^ 1];
+    const bf16x8 (&pold)[kQB][2] = pbuf[B ^ 1];
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) snext[qb][r] = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      // operands of the next chunk (or of the next step's first chunk)
+      if (ch + 1 < NCH) {
+        kop[(ch + 1) & 1] = read_k(sk_next, ch + 1);
+        vop[(ch + 1) & 1] = read_v(sv_pv, ch + 1);
+      } else {
+        kop[0] = read_k(sk_next == kSlots - 1 ? 0 : sk_next + 1, 0);
+        vop[0] = read_v(sv_next, 0);
+      }
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) snext[qb] = mfma(kop[ch & 1], qf[qb][ch], snext[qb]);
+      {
+        const int db = ch % DB, mm = ch / DB;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) oacc[db][qb] = mfma(vop[ch & 1], pold[qb][mm], oacc[db][qb]);
+      }
+      softmax_slice<GUARD>(ch, B, t);
+      if (ch == 1) {
+        store_tile(kslot + sk_w * Ly::KSLOT, Ly::KS, stg_k);
+        store_tile(vslot + sv_w * Ly::VSLOT, Ly::VS, stg_v);
+      }
+      if (ch == 2) {
+        load_tile<GUARD>(kg, t + 4, stg_k);
+        load_tile<GUARD>(vg, t + 2, stg_v);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // deferred correction of O for rows whose shift moved
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) any |= alpha[qb] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha[qb];
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(oacc[db][qb]));
+    }
+    __syncthreads();
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int BH, int N, int nQB, float c) {
-  constexpr int W = 32 * QB;    // queries per wavefront
-  constexpr int BR = kWaves * W;  // queries per workgroup
-  constexpr int KB = kBc / 32;  // 32-key blocks per tile
-  constexpr int DK = D / 16;    // k-steps of the first product
-  constexpr int DB = D / 32;    // 32-column blocks of O^T
-  using S = Smem<D>;
-  __shared__ __attribute__((aligned(16))) S sm;
+    uint16_t* __restrict__ o, float* __restrict__ lse, int BH, int N, int nQB, float c, uint32_t qxor,
+    uint32_t qand) {
+  using A = Attn<D, CAUSAL>;
+  using Ly = typename A::Ly;
+  constexpr int DK = A::DK, DB = A::DB;
+  __shared__ __attribute__((aligned(16))) char smem[Ly::BYTES];
 
+  A s;
+  // work item -> (query block, head): heaviest causal blocks first; consecutive
+  // ids go to different XCDs, so with B*H a multiple of 8 all blocks of a head
+  // share one XCD's L2
   const int L = blockIdx.x;
   const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
   const int bh = L % BH;
-  const size_t base = (size_t)bh * N * D;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, li = lane & 31;
-  const int q0 = qblk * BR;
-  const int qw0 = q0 + wave * W;
-  const bool cpos = c >= 0.f;
+  s.kg = k;
+  s.vg = v;
+  s.kslot = smem;
+  s.vslot = smem + kSlots * Ly::KSLOT;
+  s.base = (size_t)bh * N * D;
+  s.N = N;
+  s.tid = threadIdx.x;
+  s.lane = s.tid & 63;
+  s.g = s.lane >> 5;
+  s.li = s.lane & 31;
+  const int q0 = qblk * kBr;
+  s.qw0 = q0 + (s.tid >> 6) * kW;
+  s.c = c;
+  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
+  const int nT = (kv_end + kBc - 1) / kBc;
+  // tiles 0 .. nFull-1 hold only keys that every query of the workgroup sees
+  const int nFull = (CAUSAL ? min(N, q0 + 1) : N) / kBc;
 
-  // Q^T as B operand: lane holds 8 consecutive d of its query per k-step.
-  bf16x8 qf[QB][DK];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + li;
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int row = s.qw0 + qb * 32 + s.li;
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
       uint4 val = make_uint4(0, 0, 0, 0);
-      if (row < N) val = *reinterpret_cast<const uint4*>(q + base + (size_t)row * D + ks * 16 + g * 8);
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, val);
+      if (row < N) val = *reinterpret_cast<const uint4*>(q + s.base + (size_t)row * D + ks * 16 + s.g * 8);
+      // scale < 0: every sign bit flipped; scale == 0: zeros (c is then 1)
+      val = make_uint4((val.x ^ qxor) & qand, (val.y ^ qxor) & qand, (val.z ^ qxor) & qand,
+                       (val.w ^ qxor) & qand);
+      s.qf[qb][ks] = __builtin_bit_cast(bf16x8, val);
     }
-  }
-
-  f32x16 oacc[DB][QB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m[qb] = -kInf; l[qb] = 0.f; }
-
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int nT = (kv_end + kBc - 1) / kBc;
-  for (int t = 0; t < nT; ++t) {
-    const int k0 = t * kBc;
-    __syncthreads();
-    // ---- K tile -> LDS (rows of d, 16-byte chunks)
-#pragma unroll
-    for (int i = 0; i < kBc * D / 8 / (kWaves * 64); ++i) {
-      const int cidx = tid + i * kWaves * 64;
-      const int row = cidx / (D / 8), col = (cidx % (D / 8)) * 8;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (k0 + row < N) val = *reinterpret_cast<const uint4*>(k + base + (size_t)(k0 + row) * D + col);
-      *reinterpret_cast<uint4*>(&sm.k[row * S::KS + col]) = val;
-    }
-    // ---- V tile -> LDS transposed (V^T: rows of keys)
-    {
-      constexpr int KPT = kBc * D / 8 / (kWaves * 64);  // keys per thread (4 for d=128, 2 for d=64)
-      const int dc = tid % (D / 8), kg = tid / (D / 8);
-      uint4 vv[KPT];
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int key = k0 + kg * KPT + j;
-        vv[j] = make_uint4(0, 0, 0, 0);
-        if (key < N) vv[j] = *reinterpret_cast<const uint4*>(v + base + (size_t)key * D + dc * 8);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t h[KPT];
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-          const uint32_t w = (&vv[j].x)[e >> 1];
-          h[j] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFF));
-        }
-        uint16_t* dst = &sm.vt[(dc * 8 + e) * S::VS + kg * KPT];
-        if constexpr (KPT == 4) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = h[0] | ((uint32_t)h[1] << 16);
-        }
-      }
-    }
-    __syncthreads();
-    if (CAUSAL && k0 > qw0 + W - 1) continue;  // every key of the tile is in this wave's future
-
-    // ---- S^T = K Q^T
-    f32x16 s[KB][QB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int row = kb * 32 + permuted_row(li);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[row * S::KS + ks * 16 + g * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax (log2 domain: t = c * s, c = scale * log2(e))
-    const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
-    bf16x8 pf[QB][kBc / 16];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qi = qw0 + qb * 32 + li;
-      // the max of c*s is c*max(s) for c >= 0 and c*min(s) for c < 0 (rounding is monotone)
-      float mx = cpos ? -kInf : kInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[kb][qb][r];
-          if (masked) {
-            const int key = k0 + kb * 32 + key_of_reg(r, g);
-            if (key >= N || (CAUSAL && key > qi)) x = cpos ? -kInf : kInf;
-          }
-          mx = cpos ? fmaxf(mx, x) : fminf(mx, x);
-        }
-      const float mo = xor32(mx);
-      mx = cpos ? fmaxf(mx, mo) : fminf(mx, mo);
-      const float mt = (mx == kInf || mx == -kInf) ? -kInf : c * mx;
-      const float m_new = fmaxf(m[qb], mt);
-      const float alpha = m_new == -kInf ? 1.f : exp2_fast(m[qb] - m_new);
-      const float msub = m_new == -kInf ? 0.f : m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = exp2_fast(fmaf(s[kb][qb][r], c, -msub));
-          if (masked) {
-            const int key = k0 + kb * 32 + key_of_reg(r, g);
-            if (key >= N || (CAUSAL && key > qi)) p = 0.f;
-          }
-          s[kb][qb][r] = p;
-          rs += p;
-        }
-      l[qb] = alpha * l[qb] + rs;
-      m[qb] = m_new;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint4 w;
-          w.x = pack_bf16x2(s[kb][qb][8 * h + 0], s[kb][qb][8 * h + 1]);
-          w.y = pack_bf16x2(s[kb][qb][8 * h + 2], s[kb][qb][8 * h + 3]);
-          w.z = pack_bf16x2(s[kb][qb][8 * h + 4], s[kb][qb][8 * h + 5]);
-          w.w = pack_bf16x2(s[kb][qb][8 * h + 6], s[kb][qb][8 * h + 7]);
-          pf[qb][kb * 2 + h] = __builtin_bit_cast(bf16x8, w);
-        }
-    }
-
-    // ---- O^T += V^T P^T
+    s.m[qb] = -kInf;
+    s.l[qb] = 0.f;
+    s.lh[qb] = 0.f;
+    s.alpha[qb] = 1.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int mm = 0; mm < kBc / 16; ++mm) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[(db * 32 + li) * S::VS + mm * 16 + g * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][mm], oacc[db][qb], 0, 0, 0);
-      }
+      for (int r = 0; r < 16; ++r) s.oacc[db][qb][r] = 0.f;
   }
+  s.pin_agprs();
+
+  // ---- prologue: K_0, K_1, K_2 and V_0 into LDS, V slot 2 (standing for V_{-1}) and
+  // P_{-1} zero; S_0; stage K_3 and V_1; operands of step 0's first chunk
+#pragma unroll 1
+  for (int j = 0; j < 3; ++j) {
+    s.template load_tile<true>(k, j, s.stg_k);
+    s.store_tile(s.kslot + j * Ly::KSLOT, Ly::KS, s.stg_k);
+  }
+  s.template load_tile<true>(v, 0, s.stg_v);
+  s.store_tile(s.vslot, Ly::VS, s.stg_v);
+#pragma unroll
+  for (int i = 0; i < Ly::CHUNKS; ++i) s.stg_v[i] = make_uint4(0, 0, 0, 0);
+  s.store_tile(s.vslot + 2 * Ly::VSLOT, Ly::VS, s.stg_v);
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) s.pbuf[1][qb][h] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  __syncthreads();
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s.sbuf[0][qb][r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) {
+    const bf16x8 a = s.read_k(0, ks);
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) s.sbuf[0][qb] = mfma(a, s.qf[qb][ks], s.sbuf[0][qb]);
+  }
+  s.template load_tile<true>(k, 3, s.stg_k);
+  s.template load_tile<true>(v, 1, s.stg_v);
+  s.kop[0] = s.read_k(1, 0);
+  s.vop[0] = s.read_v(2, 0);
+
+  // ---- steps; the slot of tile j is j % 3
+  int sk_next = 1, sk_w = 0, sv_pv = 2, sv_next = 0, sv_w = 1;  // for t = 0
+  auto advance = [&]() {
+    sk_next = sk_next == 2 ? 0 : sk_next + 1;
+    sk_w = sk_w == 2 ? 0 : sk_w + 1;
+    sv_pv = sv_pv == 2 ? 0 : sv_pv + 1;
+    sv_next = sv_next == 2 ? 0 : sv_next + 1;
+    sv_w = sv_w == 2 ? 0 : sv_w + 1;
+  };
+  // steps with 1 <= t, tiles t and t+1 unmasked and tile t + 4 inside N need
+  // neither masks nor load bounds.  Buffer parity B = t % 2 is static: every
+  // loop below starts at an odd t and advances by two.
+  const int steady_end = min(nFull - 1, N / kBc - 4);
+  s.template step<true, 0>(0, sk_next, sk_w, sv_pv, sv_next, sv_w);
+  advance();
+  int t = 1;
+  for (; t + 1 < steady_end; t += 2) {
+    s.template step<false, 1>(t, sk_next, sk_w, sv_pv, sv_next, sv_w);
+    advance();
+    s.template step<false, 0>(t + 1, sk_next, sk_w, sv_pv, sv_next, sv_w);
+    advance();
+  }
+  for (; t < nT; t += 2) {
+    s.template step<true, 1>(t, sk_next, sk_w, sv_pv, sv_next, sv_w);
+    advance();
+    if (t + 1 < nT) {
+      s.template step<true, 0>(t + 1, sk_next, sk_w, sv_pv, sv_next, sv_w);
+      advance();
+    }
+  }
+
+  // last product: O += P_{nT-1} V_{nT-1} (operands of its first chunk read by the last step)
+  if ((nT - 1) & 1) s.template last_pv<1>((nT - 1) % kSlots);
+  else s.template last_pv<0>((nT - 1) % kSlots);
 
   // ---- epilogue: the single division by the row sum, LSE, stores
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l[qb] + xor32(l[qb]);
-    const int qi = qw0 + qb * 32 + li;
+  for (int qb = 0; qb < kQB; ++qb) {
+    const float lt = s.l[qb] + xor32(s.l[qb]);
+    const float lht = s.lh[qb] + xor32(s.lh[qb]);
+    const int qi = s.qw0 + qb * 32 + s.li;
     if (qi < N) {
-      const float inv = 1.f / lt;
+      const float inv = 1.f / lht;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const int dcol = db * 32 + 8 * a4 + 4 * g;
-          uint2 w;
-          w.x = pack_bf16x2(oacc[db][qb][4 * a4 + 0] * inv, oacc[db][qb][4 * a4 + 1] * inv);
-          w.y = pack_bf16x2(oacc[db][qb][4 * a4 + 2] * inv, oacc[db][qb][4 * a4 + 3] * inv);
-          *reinterpret_cast<uint2*>(o + base + (size_t)qi * D + dcol) = w;
+          const int dcol = db * 32 + 8 * a4 + 4 * s.g;
+          uint2 wv;
+          wv.x = pack_bf16x2(s.oacc[db][qb][4 * a4 + 0] * inv, s.oacc[db][qb][4 * a4 + 1] * inv);
+          wv.y = pack_bf16x2(s.oacc[db][qb][4 * a4 + 2] * inv, s.oacc[db][qb][4 * a4 + 3] * inv);
+          *reinterpret_cast<uint2*>(o + s.base + (size_t)qi * D + dcol) = wv;
         }
-      if (g == 0) lse[(size_t)bh * N + qi] = (m[qb] + log2_fast(lt)) * kLn2;
+      if (s.g == 0) lse[(size_t)bh * N + qi] = (s.m[qb] + log2_fast(lt)) * kLn2;
     }
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const AttnArgs& a) {
-  constexpr int QB = 1;
-  constexpr int BR = kWaves * 32 * QB;
   const int BH = (int)(a.B * a.H), N = (int)a.N;
-  const int nQB = (N + BR - 1) / BR;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB>), dim3((unsigned)(nQB * BH)), dim3(kWaves * 64), 0,
+  const int nQB = (N + kBr - 1) / kBr;
+  // the kernel needs a positive multiplier c: scale * (q . k) = |scale| * ((-q) . k) for
+  // scale < 0 (negating bf16 is exact), and a zero scale is the same as zero queries
+  const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
+  const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
+  const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, BH, N, nQB,
-                     a.scale * kLog2e);
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, BH, N, nQB, c,
+                     qxor, qand);
   return hipGetLastError();
 }
 

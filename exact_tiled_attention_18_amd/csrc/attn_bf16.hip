@@ -65,26 +65,23 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kQB = 2;            // 32-query blocks per wavefront
-constexpr int kW = 32 * kQB;      // queries per wavefront
-constexpr int kBr = kWaves * kW;  // queries per workgroup
 constexpr int kBc = 32;           // keys per tile
 constexpr int kSlots = 3;         // LDS slots per operand
-constexpr int kThreads = kWaves * 64;
 constexpr float kRescaleSlack = 8.f;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-template <int D>
+template <int D, int kThreads>
 struct Layout {
   static constexpr int KS = D * 2 + 16;  // K row stride (bytes): conflict-free 16-byte row reads
   static constexpr int VS = D * 2 + 64;  // V row stride (bytes): conflict-free transposing reads
   static constexpr int KSLOT = kBc * KS;
   static constexpr int VSLOT = kBc * VS;
   static constexpr int BYTES = kSlots * (KSLOT + VSLOT);
-  static constexpr int CHUNKS = kBc * D * 2 / 16 / kThreads;  // 16-byte copies per thread per operand tile
+  static constexpr int PIECES = kBc * D * 2 / 16;                      // 16-byte pieces per operand tile
+  static constexpr int CHUNKS = PIECES >= kThreads ? PIECES / kThreads : 1;  // pieces per thread
+  static constexpr bool PARTIAL = PIECES < kThreads;  // only the first PIECES threads copy
 };
 
 __device__ __forceinline__ int permuted_row(int i) { return i ^ ((((i >> 2) ^ (i >> 3)) & 1) * 0xC); }
@@ -99,9 +96,18 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool CAUSAL>
+// QB = 32-query blocks per wavefront.  QB = 1: 8 wavefronts, two per SIMD, whose
+// instruction streams the SIMD interleaves (one wavefront alone issues vector
+// instructions at about a third of the SIMD's rate).  QB = 2: 4 wavefronts, one
+// per SIMD, each with the whole register file.  Both own 256 queries per workgroup.
+template <int D, bool CAUSAL, int QB>
 struct Attn {
-  using Ly = Layout<D>;
+  static constexpr int kQB = QB;
+  static constexpr int kWaves = QB == 1 ? 8 : 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kW = 32 * kQB;
+  static constexpr int kBr = kWaves * kW;
+  using Ly = Layout<D, kThreads>;
   static constexpr int DK = D / 16;  // k-steps of S = chunks per step
   static constexpr int DB = D / 32;  // 32-row blocks of O^T
   static constexpr int NCH = DK;     // chunks per step; PV chunk ch is (db, mm) = (ch % DB, ch / DB)
@@ -117,13 +123,18 @@ struct Attn {
   float m[kQB], l[kQB], lh[kQB], alpha[kQB], msub[kQB], mx[kQB], rs[kQB];
 
   // ---- per-workgroup constants
-  const uint16_t* kg;
-  const uint16_t* vg;
+  __amdgpu_buffer_rsrc_t krs, vrs;  // this head's K and V; reads past N return zeros
   char* kslot;
   char* vslot;
-  size_t base;
-  int N, qw0, lane, g, li, tid;
-  float c;  // > 0: scale * log2(e) in magnitude
+  int N, qw0, lane, g, li;
+  int ld_off;   // byte offset of this thread's first 16-byte piece inside a tile
+  int kst_off;  // LDS byte offset of that piece in a K slot
+  int vst_off;  // ... in a V slot
+  int krd_off;  // LDS byte offset of this lane's K operand row (k-step 0) in a slot
+  int vrd_off;  // LDS byte offset of this lane's V^T operand (chunk 0) in a slot
+  bool copier;  // this thread moves tile pieces (all threads unless a tile has fewer pieces)
+  float c;      // > 0: scale * log2(e) in magnitude
+  static constexpr int kRowsPerPiece = kThreads / (D / 8);  // rows between a thread's pieces (CHUNKS > 1)
 
   // Register-class hints (empty asm, no instructions): Q fragments and the O
   // accumulators live in AGPRs -- only MFMAs read them -- leaving the
@@ -132,61 +143,42 @@ struct Attn {
   __device__ __forceinline__ void pin_agprs() {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
+      if (kQB == 2) {  // with one query block the allocator keeps them in VGPRs
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
+        for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(oacc[db][qb]));
     }
   }
 
   __device__ __forceinline__ bf16x8 read_k(int slot, int ks) const {
-    return *reinterpret_cast<const bf16x8*>(kslot + slot * Ly::KSLOT + permuted_row(li) * Ly::KS + g * 16 +
-                                            ks * 32);
+    return *reinterpret_cast<const bf16x8*>(kslot + slot * Ly::KSLOT + krd_off + ks * 32);
   }
   __device__ __forceinline__ bf16x8 read_v(int slot, int ch) const {
     const int db = ch % DB, mm = ch / DB;
-    const int grp16 = lane >> 4, l16 = lane & 15;
-    const char* pa = vslot + slot * Ly::VSLOT + (mm * 16 + 8 * (grp16 >> 1) + (l16 >> 2)) * Ly::VS +
-                     (db * 32 + 16 * (grp16 & 1) + 4 * (l16 & 3)) * 2;
+    const char* pa = vslot + slot * Ly::VSLOT + vrd_off + (mm * 16) * Ly::VS + db * 64;
     const v4i16 lo = tr_read(pa), hi = tr_read(pa + 4 * Ly::VS);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  // thread index as an opaque value: the copy addresses derived from it are
-  // recomputed in every step (a few integer ops) instead of being hoisted out of
-  // the tile loop, where they would occupy registers across the whole loop
-  __device__ __forceinline__ int fresh_tid() const {
-    int x = tid;
-    asm volatile("" : "+v"(x));
-    return x;
-  }
-  // piece i of a tile copy covers row  tid / (D/8) + i * (kThreads / (D/8)),  column  8 * (tid % (D/8))
-
-  // ---- HBM -> registers -> LDS copies of one operand tile (16-byte pieces, coalesced rows)
-  template <bool GUARD>
-  __device__ __forceinline__ void load_tile(const uint16_t* src, int t, uint4 (&stg)[Ly::CHUNKS]) const {
-    const int ft = fresh_tid();
-    const int row0 = ft / (D / 8), col = (ft % (D / 8)) * 8;
-#pragma unroll
-    for (int i = 0; i < Ly::CHUNKS; ++i) {
-      const int row = row0 + i * (kThreads / (D / 8));
-      const int key = t * kBc + row;
-      if (!GUARD) {
-        stg[i] = *reinterpret_cast<const uint4*>(src + base + (size_t)key * D + col);
-      } else {
-        // rows past N: read a valid row and replace it by zeros (no branch)
-        const uint4 x = *reinterpret_cast<const uint4*>(src + base + (size_t)min(key, N - 1) * D + col);
-        const bool in = key < N;
-        stg[i] = make_uint4(in ? x.x : 0u, in ? x.y : 0u, in ? x.z : 0u, in ? x.w : 0u);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_tile(char* dst, int stride, const uint4 (&stg)[Ly::CHUNKS]) const {
-    const int ft = fresh_tid();
-    char* p = dst + (ft / (D / 8)) * stride + (ft % (D / 8)) * 16;
+  // ---- HBM -> registers -> LDS copies of one operand tile: 16-byte pieces, rows read
+  // whole (coalesced); piece i of a thread is row tid/(D/8) + i*kRowsPerPiece.
+  // Buffer loads return zeros for rows past N (the whole offset is in the VGPR
+  // operand, which the hardware bounds check covers).
+  __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, int t, uint4 (&stg)[Ly::CHUNKS]) const {
+    if (Ly::PARTIAL && !copier) return;
 #pragma unroll
     for (int i = 0; i < Ly::CHUNKS; ++i)
-      *reinterpret_cast<uint4*>(p + i * (kThreads / (D / 8)) * stride) = stg[i];
+      stg[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, ld_off + (t * kBc + i * kRowsPerPiece) * D * 2, 0, 0));
+  }
+  __device__ __forceinline__ void store_tile(char* slot_base, int off, int stride,
+                                             const uint4 (&stg)[Ly::CHUNKS]) const {
+    if (Ly::PARTIAL && !copier) return;
+    char* p = slot_base + off;
+#pragma unroll
+    for (int i = 0; i < Ly::CHUNKS; ++i) *reinterpret_cast<uint4*>(p + i * kRowsPerPiece * stride) = stg[i];
   }
 
   // ---- softmax of the scores in sbuf[B] (tile t) -> pbuf[B].  The launcher
@@ -249,38 +241,33 @@ struct Attn {
     lh[qb] = h_acc;
     l[qb] += rs[qb];
   }
-  // slice ch of the softmax work (mask, row max, shift, 32 exponentials, packing)
+  // slice ch of the softmax work: mask and row max, shift, the 16*kQB exponentials
+  // spread over the middle chunks, packing at the end
   template <bool GUARD>
   __device__ __forceinline__ void softmax_slice(int ch, int B, int t) {
-    if (NCH == 8) {
-      switch (ch) {
-        case 0:
-          if (GUARD) mask_scores(B, t);
-          row_max(B, 0);
-          row_max(B, 1);
-          break;
-        case 1: new_shift(0); new_shift(1); break;
-        case 2: exps(B, 0, 7); break;
-        case 3: exps(B, 7, 14); break;
-        case 4: exps(B, 14, 21); break;
-        case 5: exps(B, 21, 28); break;
-        case 6: exps(B, 28, 32); pack(B, 0); break;
-        default: pack(B, 1); break;
-      }
-    } else {
-      switch (ch) {
-        case 0:
-          if (GUARD) mask_scores(B, t);
-          row_max(B, 0);
-          row_max(B, 1);
-          new_shift(0);
-          new_shift(1);
-          break;
-        case 1: exps(B, 0, 16); break;
-        case 2: exps(B, 16, 32); pack(B, 0); break;
-        default: pack(B, 1); break;
+    constexpr int E = 16 * kQB;
+    constexpr int first_exp = NCH == 8 ? 2 : 1;       // chunks [first_exp, last_exp) hold exponentials
+    constexpr int last_exp = NCH == 8 ? 6 : 3;
+    constexpr int per = (E + (last_exp - first_exp) - 1) / (last_exp - first_exp);
+    if (ch == 0) {
+      if (GUARD) mask_scores(B, t);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) row_max(B, qb);
+      if (NCH != 8) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) new_shift(qb);
       }
     }
+    if (NCH == 8 && ch == 1) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) new_shift(qb);
+    }
+    if (ch >= first_exp && ch < last_exp) {
+      const int e0 = (ch - first_exp) * per;
+      exps(B, e0, e0 + per < E ? e0 + per : E);
+    }
+    if (ch == NCH - 2) pack(B, 0);
+    if (ch == NCH - 1 && kQB == 2) pack(B, 1);
   }
 
   template <int B>
@@ -296,9 +283,8 @@ struct Attn {
 
   // ---- one pipeline step for tile t: S_{t+1} into sbuf[B^1], O += P_{t-1} V_{t-1},
   // softmax of sbuf[B] -> pbuf[B]; LDS writes of K_{t+3}, V_{t+1}; loads of K_{t+4}, V_{t+2}.
-  // GUARD steps (the first, the causal diagonal and the tail) mask scores and bound
-  // the tile loads; the others (1 <= t, tiles t, t+1 unmasked, tile t + 4 inside N)
-  // need neither.
+  // GUARD steps (the first, the causal diagonal and the tail) mask scores; the
+  // others (1 <= t, tiles t and t+1 unmasked) need no mask.
   template <bool GUARD, int B>
   __device__ __forceinline__ void step(int t, int sk_next, int sk_w, int sv_pv, int sv_next, int sv_w) {
     f32x16 (&snext)[kQB] = sbuf[B ^ 1];
@@ -326,13 +312,26 @@ struct Attn {
       }
       softmax_slice<GUARD>(ch, B, t);
       if (ch == 1) {
-        store_tile(kslot + sk_w * Ly::KSLOT, Ly::KS, stg_k);
-        store_tile(vslot + sv_w * Ly::VSLOT, Ly::VS, stg_v);
+        store_tile(kslot + sk_w * Ly::KSLOT, kst_off, Ly::KS, stg_k);
+        store_tile(vslot + sv_w * Ly::VSLOT, vst_off, Ly::VS, stg_v);
       }
       if (ch == 2) {
-        load_tile<GUARD>(kg, t + 4, stg_k);
-        load_tile<GUARD>(vg, t + 2, stg_v);
+        load_tile(krs, t + 4, stg_k);
+        load_tile(vrs, t + 2, stg_v);
       }
+      // issue order inside the chunk: the next chunk's LDS reads, then each MFMA
+      // followed by a run of vector instructions (in-order issue would otherwise
+      // stall the vector work behind back-to-back MFMAs), then memory copies
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 200, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);  // DS writes
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // VMEM reads
       __builtin_amdgcn_sched_barrier(0);
     }
     // deferred correction of O for rows whose shift moved
@@ -355,14 +354,14 @@ struct Attn {
   }
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
+template <int D, bool CAUSAL, int QB>
+__global__ __launch_bounds__(QB == 1 ? 512 : 256) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int BH, int N, int nQB, float c, uint32_t qxor,
     uint32_t qand) {
-  using A = Attn<D, CAUSAL>;
+  using A = Attn<D, CAUSAL, QB>;
   using Ly = typename A::Ly;
-  constexpr int DK = A::DK, DB = A::DB;
+  constexpr int DK = A::DK, DB = A::DB, kQB = A::kQB, kW = A::kW, kBr = A::kBr, kThreads = A::kThreads;
   __shared__ __attribute__((aligned(16))) char smem[Ly::BYTES];
 
   A s;
@@ -372,18 +371,29 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
   const int L = blockIdx.x;
   const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
   const int bh = L % BH;
-  s.kg = k;
-  s.vg = v;
+  const size_t base = (size_t)bh * N * D;
+  constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9-class GPUs
+  s.krs = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, N * D * 2, kRsrcWord3);
+  s.vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, N * D * 2, kRsrcWord3);
   s.kslot = smem;
   s.vslot = smem + kSlots * Ly::KSLOT;
-  s.base = (size_t)bh * N * D;
   s.N = N;
-  s.tid = threadIdx.x;
-  s.lane = s.tid & 63;
+  const int tid = threadIdx.x;
+  s.lane = tid & 63;
   s.g = s.lane >> 5;
   s.li = s.lane & 31;
+  {
+    s.copier = tid < Ly::PIECES;
+    const int prow = (tid % Ly::PIECES) / (D / 8), pcol = (tid % (D / 8)) * 16;  // first piece: row, byte column
+    s.ld_off = prow * D * 2 + pcol;
+    s.kst_off = prow * Ly::KS + pcol;
+    s.vst_off = prow * Ly::VS + pcol;
+    s.krd_off = permuted_row(s.li) * Ly::KS + s.g * 16;
+    const int grp16 = s.lane >> 4, l16 = s.lane & 15;
+    s.vrd_off = (8 * (grp16 >> 1) + (l16 >> 2)) * Ly::VS + (16 * (grp16 & 1) + 4 * (l16 & 3)) * 2;
+  }
   const int q0 = qblk * kBr;
-  s.qw0 = q0 + (s.tid >> 6) * kW;
+  s.qw0 = q0 + (tid >> 6) * kW;
   s.c = c;
   const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
   const int nT = (kv_end + kBc - 1) / kBc;
@@ -396,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
       uint4 val = make_uint4(0, 0, 0, 0);
-      if (row < N) val = *reinterpret_cast<const uint4*>(q + s.base + (size_t)row * D + ks * 16 + s.g * 8);
+      if (row < N) val = *reinterpret_cast<const uint4*>(q + base + (size_t)row * D + ks * 16 + s.g * 8);
       // scale < 0: every sign bit flipped; scale == 0: zeros (c is then 1)
       val = make_uint4((val.x ^ qxor) & qand, (val.y ^ qxor) & qand, (val.z ^ qxor) & qand,
                        (val.w ^ qxor) & qand);
@@ -417,14 +427,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
   // P_{-1} zero; S_0; stage K_3 and V_1; operands of step 0's first chunk
 #pragma unroll 1
   for (int j = 0; j < 3; ++j) {
-    s.template load_tile<true>(k, j, s.stg_k);
-    s.store_tile(s.kslot + j * Ly::KSLOT, Ly::KS, s.stg_k);
+    s.load_tile(s.krs, j, s.stg_k);
+    s.store_tile(s.kslot + j * Ly::KSLOT, s.kst_off, Ly::KS, s.stg_k);
   }
-  s.template load_tile<true>(v, 0, s.stg_v);
-  s.store_tile(s.vslot, Ly::VS, s.stg_v);
+  s.load_tile(s.vrs, 0, s.stg_v);
+  s.store_tile(s.vslot, s.vst_off, Ly::VS, s.stg_v);
 #pragma unroll
   for (int i = 0; i < Ly::CHUNKS; ++i) s.stg_v[i] = make_uint4(0, 0, 0, 0);
-  s.store_tile(s.vslot + 2 * Ly::VSLOT, Ly::VS, s.stg_v);
+  s.store_tile(s.vslot + 2 * Ly::VSLOT, s.vst_off, Ly::VS, s.stg_v);
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
@@ -440,8 +450,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) s.sbuf[0][qb] = mfma(a, s.qf[qb][ks], s.sbuf[0][qb]);
   }
-  s.template load_tile<true>(k, 3, s.stg_k);
-  s.template load_tile<true>(v, 1, s.stg_v);
+  s.load_tile(s.krs, 3, s.stg_k);
+  s.load_tile(s.vrs, 1, s.stg_v);
   s.kop[0] = s.read_k(1, 0);
   s.vop[0] = s.read_v(2, 0);
 
@@ -454,10 +464,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
     sv_next = sv_next == 2 ? 0 : sv_next + 1;
     sv_w = sv_w == 2 ? 0 : sv_w + 1;
   };
-  // steps with 1 <= t, tiles t and t+1 unmasked and tile t + 4 inside N need
-  // neither masks nor load bounds.  Buffer parity B = t % 2 is static: every
-  // loop below starts at an odd t and advances by two.
-  const int steady_end = min(nFull - 1, N / kBc - 4);
+  // steps with 1 <= t and tiles t, t+1 unmasked need no mask.  Buffer parity
+  // B = t % 2 is static: every loop below starts at an odd t and advances by two.
+  const int steady_end = nFull - 1;
   s.template step<true, 0>(0, sk_next, sk_w, sv_pv, sv_next, sv_w);
   advance();
   int t = 1;
@@ -496,15 +505,17 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(
           uint2 wv;
           wv.x = pack_bf16x2(s.oacc[db][qb][4 * a4 + 0] * inv, s.oacc[db][qb][4 * a4 + 1] * inv);
           wv.y = pack_bf16x2(s.oacc[db][qb][4 * a4 + 2] * inv, s.oacc[db][qb][4 * a4 + 3] * inv);
-          *reinterpret_cast<uint2*>(o + s.base + (size_t)qi * D + dcol) = wv;
+          *reinterpret_cast<uint2*>(o + base + (size_t)qi * D + dcol) = wv;
         }
       if (s.g == 0) lse[(size_t)bh * N + qi] = (s.m[qb] + log2_fast(lt)) * kLn2;
     }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int QB>
 hipError_t launch(const AttnArgs& a) {
+  constexpr int kBr = Attn<D, CAUSAL, QB>::kBr;
+  constexpr int kThreads = Attn<D, CAUSAL, QB>::kThreads;
   const int BH = (int)(a.B * a.H), N = (int)a.N;
   const int nQB = (N + kBr - 1) / kBr;
   // the kernel needs a positive multiplier c: scale * (q . k) = |scale| * ((-q) . k) for
@@ -512,7 +523,7 @@ hipError_t launch(const AttnArgs& a) {
   const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
   const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB>), dim3((unsigned)(nQB * BH)), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, BH, N, nQB, c,
                      qxor, qand);
@@ -521,9 +532,14 @@ hipError_t launch(const AttnArgs& a) {
 
 }  // namespace
 
+#ifndef FA_BF16_QB
+#define FA_BF16_QB 1
+#endif
+
 hipError_t launch_attn_bf16(const AttnArgs& a) {
-  if (a.d == 64) return a.causal ? launch<64, true>(a) : launch<64, false>(a);
-  return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+  constexpr int QB = FA_BF16_QB;
+  if (a.d == 64) return a.causal ? launch<64, true, QB>(a) : launch<64, false, QB>(a);
+  return a.causal ? launch<128, true, QB>(a) : launch<128, false, QB>(a);
 }
 
 }  // namespace fa

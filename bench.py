@@ -66,6 +66,74 @@ def algorithmic_bytes(w) -> float:
     return 3 * n + scales + 2 * n + lse
 
 
+def copy_calibration(mib: int, dev) -> None:
+    """A plain device-to-device copy of known size (mib MiB read, mib MiB written),
+    launched a few times so that a counter pass over this program can relate
+    FETCH_SIZE / WRITE_SIZE to bytes actually moved."""
+    x = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+
+
+def _counter_rows(path: str):
+    import csv
+    if os.path.isdir(path):
+        found = [os.path.join(r, f) for r, _, fs in os.walk(path) for f in fs if f.endswith("counter_collection.csv")]
+        if len(found) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {path}, found {found}")
+        path = found[0]
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _mean_counter(rows, counter: str, pick) -> tuple[float, int]:
+    per_dispatch = {}
+    for r in rows:
+        if r["Counter_Name"] == counter and pick(r):
+            per_dispatch[r["Dispatch_Id"]] = per_dispatch.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per_dispatch:
+        raise SystemExit(f"no {counter} rows for the requested kernel")
+    return sum(per_dispatch.values()) / len(per_dispatch), len(per_dispatch)
+
+
+def write_traffic(workload: str, fetch_path: str, write_path: str, copy_mib: int, commands: list[str]) -> dict:
+    """HBM bytes per launch of the attention kernel from two rocprofv3 counter
+    passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for the plain copy of copy_mib MiB in the same program."""
+    w = synthetic.workload(workload)
+    attn_tag = {"bf16": "attn_fwd_bf16_kernel", "f32": "attn_fwd_f32_kernel", "fp8": "attn_fwd_fp8_kernel"}[w.dtype]
+    is_attn = lambda r: attn_tag in r["Kernel_Name"]  # noqa: E731
+    known = float(copy_mib << 20)
+    out = {"workload": workload, "kernel": attn_tag,
+           "kernel_source_sha": source_sha(KERNEL_SOURCE[w.dtype]), "copy_bytes": known, "commands": commands}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
+        rows = _counter_rows(path)
+        # the calibration copies are the runtime's buffer-copy kernel at its largest grid
+        # (other, small copies of the same kernel move the inputs of the run)
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit(f"no buffer-copy dispatches in {path}")
+        grid = max(int(r["Grid_Size"]) for r in copies)
+        is_copy = lambda r, g=grid: "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == g  # noqa: E731
+        kib, n = _mean_counter(rows, counter, is_attn)
+        ckib, cn = _mean_counter(rows, counter, is_copy)
+        factor = known / (ckib * 1024.0)
+        out[counter] = {"kernel_kib_per_dispatch": kib, "kernel_dispatches": n, "copy_kib_per_dispatch": ckib,
+                        "copy_dispatches": cn, "factor": factor, "bytes_per_launch": kib * 1024.0 * factor}
+        total += kib * 1024.0 * factor
+    out["bytes_per_launch"] = total
+    out["algorithmic_bytes_per_launch"] = algorithmic_bytes(w)
+    dst = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(dst, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    return out
+
+
 def make_step(fa, w, dev):
     q, k, v, signs = synthetic.workload_inputs(w)
     q, k, v = q.to(dev), k.to(dev), v.to(dev)
@@ -122,18 +190,18 @@ def cpu_baseline(w, budget_s: float):
         threads = 1
     q, k, v, _ = synthetic.workload_inputs(w)
     heads = 0
+    nbh = w.B * w.H
     t0 = time.perf_counter()
-    for bh in range(w.B * w.H):
-        b, h = divmod(bh, w.H)
+    while time.perf_counter() - t0 < budget_s:  # cycle over the heads until the budget is spent
+        b, h = divmod(heads % nbh, w.H)
         sl = (slice(b, b + 1), slice(h, h + 1))
         A.reference(q[sl], k[sl], v[sl], w.causal, w.scale)
         heads += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
     dt = time.perf_counter() - t0
-    flops = w.flops() * heads / (w.B * w.H)
+    flops = w.flops() * heads / nbh
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads of {w.name}, full N x N fp64 oracle, {dt:.1f} s"}
+            "sample": f"{heads} head evaluations ({heads / nbh:.2f} passes over the {nbh} heads) of {w.name}, "
+                      f"full N x N fp64 oracle, {dt:.1f} s"}
 
 
 def main():
@@ -145,7 +213,19 @@ def main():
                     choices=[w.name for w in synthetic.WORKLOADS])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain copy of this many MiB (for counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc outputs into profiles/traffic_<workload>.json")
+    ap.add_argument("--traffic-command", action="append", default=[],
+                    help="with --traffic-from: the profiler command lines, recorded in the JSON")
     args = ap.parse_args()
+    if args.traffic_from:
+        if args.copy_calibration_mib <= 0:
+            raise SystemExit("--traffic-from needs --copy-calibration-mib (the size the counter runs copied)")
+        rec = write_traffic(args.workload, *args.traffic_from, args.copy_calibration_mib, args.traffic_command)
+        print(json.dumps(rec), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards heads and "
               "batches across GPUs with no exchange, so run it per GPU", file=sys.stderr)
@@ -156,6 +236,8 @@ def main():
     fa.load_library()
     dev = "cuda:0"
     w = synthetic.workload(args.workload)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(args.copy_calibration_mib, dev)
     step, parts = make_step(fa, w, dev)
     for _ in range(args.warmup):
         step()

@@ -15,7 +15,7 @@
 // follows the FlashAttention-3 ideas (same page, section 1; news page on
 // FlashAttention-3, section "Innovationen"), rebuilt for CDNA4 below.
 //
-// Wavefront layout.  A wavefront owns 64 queries (two blocks of 32).  Scores
+// Wavefront layout.  A wavefront owns 32 * QB queries (QB blocks of 32).  Scores
 // are computed transposed, S^T = K Q^T, with K as the MFMA A operand (from
 // LDS) and Q as the B operand (registers, loaded once).  In the 32x32
 // accumulator layout a lane then holds one query (lane % 32) and 16 of the 32
@@ -27,12 +27,14 @@
 // operand registers with one bf16 conversion.  O^T keeps the query-per-lane
 // layout, so rescaling it is lane-local.  V stays row-major in LDS; its
 // transposed A operand comes from the transposing read ds_read_b64_tr_b16.
-// Owning 64 queries per wavefront halves the LDS bytes read per MFMA compared
-// with 32, which keeps LDS bandwidth below the matrix-core rate.
+// The default is QB = 1 with two wavefronts per SIMD: one wavefront alone
+// issues dependent vector instructions at about a third of the SIMD's rate,
+// and the second one's stream fills the gaps.  QB = 2 (one wavefront per
+// SIMD, 64 queries) halves the LDS bytes per MFMA instead; it measured slower.
 //
-// Software pipeline.  One wavefront per SIMD, so each has the whole 512-entry
-// register file: Q fragments and O accumulators sit in AGPRs (only MFMAs read
-// them), scores, probabilities and staging in VGPRs.  Step t (one 32-key
+// Software pipeline.  O accumulators sit in AGPRs (only MFMAs read them), and
+// with QB = 2 the Q fragments too; scores, probabilities and staging are in
+// VGPRs.  Step t (one 32-key
 // tile) issues the 16 MFMAs of S_{t+1} = K_{t+1} Q^T, the 16 MFMAs of
 // O^T += V_{t-1}^T P_{t-1}^T and the vector work of the softmax of S_t.  None
 // depends on another, so the step is cut into D/16 chunks, each holding 2 + 2

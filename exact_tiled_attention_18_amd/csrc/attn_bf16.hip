@@ -32,9 +32,11 @@
 // and the second one's stream fills the gaps.  QB = 2 (one wavefront per
 // SIMD, 64 queries) halves the LDS bytes per MFMA instead; it measured slower.
 //
-// Software pipeline.  O accumulators sit in AGPRs (only MFMAs read them), and
-// with QB = 2 the Q fragments too; scores, probabilities and staging are in
-// VGPRs.  Step t (one 32-key
+// Software pipeline.  With QB = 1 the kernel fits in 256 architectural VGPRs
+// (two wavefronts per SIMD), so no value is pinned to the accumulation
+// registers: the compiler then selects the VGPR forms of the MFMAs and gives
+// the whole budget to VGPRs, with no copies between the two register files.
+// Step t (one 32-key
 // tile) issues the 16 MFMAs of S_{t+1} = K_{t+1} Q^T, the 16 MFMAs of
 // O^T += V_{t-1}^T P_{t-1}^T and the vector work of the softmax of S_t.  None
 // depends on another, so the step is cut into D/16 chunks, each holding 2 + 2
@@ -137,22 +139,6 @@ struct Attn {
   bool copier;  // this thread moves tile pieces (all threads unless a tile has fewer pieces)
   float c;      // > 0: scale * log2(e) in magnitude
   static constexpr int kRowsPerPiece = kThreads / (D / 8);  // rows between a thread's pieces (CHUNKS > 1)
-
-  // Register-class hints (empty asm, no instructions): Q fragments and the O
-  // accumulators live in AGPRs -- only MFMAs read them -- leaving the
-  // architectural VGPRs to the scores, probabilities and staging that the
-  // vector unit works on.
-  __device__ __forceinline__ void pin_agprs() {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      if (kQB == 2) {  // with one query block the allocator keeps them in VGPRs
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+a"(qf[qb][ks]));
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(oacc[db][qb]));
-    }
-  }
 
   __device__ __forceinline__ bf16x8 read_k(int slot, int ks) const {
     return *reinterpret_cast<const bf16x8*>(kslot + slot * Ly::KSLOT + krd_off + ks * 32);
@@ -347,10 +333,6 @@ struct Attn {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha[qb];
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(oacc[db][qb]));
     }
     __syncthreads();
   }
@@ -423,7 +405,6 @@ __global__ __launch_bounds__(QB == 1 ? 512 : 256) void attn_fwd_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) s.oacc[db][qb][r] = 0.f;
   }
-  s.pin_agprs();
 
   // ---- prologue: K_0, K_1, K_2 and V_0 into LDS, V slot 2 (standing for V_{-1}) and
   // P_{-1} zero; S_0; stage K_3 and V_1; operands of step 0's first chunk

@@ -148,7 +148,7 @@ def make_step(fa, w, dev):
     nt = (w.N + 127) // 128
     q8 = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
     k8 = torch.empty_like(q8)
-    v8t = torch.empty((w.B, w.H, w.d, w.N), dtype=torch.uint8, device=dev)
+    v8t = torch.empty((w.B, w.H, w.d, fa.vt_cols(w.N)), dtype=torch.uint8, device=dev)
     qs, ks, vs = (torch.empty((w.B, w.H, nt), dtype=torch.float32, device=dev) for _ in range(3))
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)

@@ -22,6 +22,11 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_SCALE, FA_ERR_ALIAS
 FA_F32, FA_BF16 = 0, 1
 TILE_ROWS = 128  # rows per fp8 quantisation tile
 
+
+def vt_cols(n: int) -> int:
+    """Row length of transposed V codes: n rounded up to a multiple of 64 (FA_FP8_VT_COLS)."""
+    return (n + 63) // 64 * 64
+
 _lib = None
 
 
@@ -83,6 +88,12 @@ def _check_dense(*ts):
             raise ValueError("tensors must be contiguous device tensors")
 
 
+def _expect(t, shape, dtype, name):
+    """The library trusts the sizes it is given: every buffer must have exactly this shape."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
 def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, lse=None, stream=None):
     """O, LSE = attention(q, k, v) for [B, H, N, d] float32 or bfloat16 tensors."""
     B, H, N, d = q.shape
@@ -94,6 +105,9 @@ def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, ls
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _check_dense(q, k, v, o, lse)
+    for t, name in ((k, "k"), (v, "v"), (o, "o")):
+        _expect(t, q.shape, q.dtype, name)
+    _expect(lse, (B, H, N), torch.float32, "lse")
     lib = load_library()
     _check(lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(causal),
                       float(scale), dtype, _stream(stream)))
@@ -103,11 +117,17 @@ def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, ls
 def fa_quant_rotate_fp8(x, signs=None, transpose_out: bool = False, x8=None, x_scale=None, stream=None):
     """e4m3 codes (uint8) and per-128-row-tile scales of x (bfloat16 [B, H, N, d])."""
     B, H, N, d = x.shape
+    x8_shape = (B, H, d, vt_cols(N)) if transpose_out else (B, H, N, d)
     if x8 is None:
-        x8 = torch.empty((B, H, d, N) if transpose_out else (B, H, N, d), dtype=torch.uint8, device=x.device)
+        x8 = torch.empty(x8_shape, dtype=torch.uint8, device=x.device)
     if x_scale is None:
         x_scale = torch.empty((B, H, (N + TILE_ROWS - 1) // TILE_ROWS), dtype=torch.float32, device=x.device)
     _check_dense(x, signs, x8, x_scale)
+    _expect(x, (B, H, N, d), torch.bfloat16, "x")
+    _expect(x8, x8_shape, torch.uint8, "x8")
+    _expect(x_scale, (B, H, (N + TILE_ROWS - 1) // TILE_ROWS), torch.float32, "x_scale")
+    if signs is not None:
+        _expect(signs, (d,), torch.int8, "signs")
     lib = load_library()
     _check(lib.fa_quant_rotate_fp8(_ptr(x), _ptr(x8), _ptr(x_scale), _ptr(signs), B, H, N, d,
                                    int(transpose_out), _stream(stream)))
@@ -116,7 +136,7 @@ def fa_quant_rotate_fp8(x, signs=None, transpose_out: bool = False, x8=None, x_s
 
 def fa_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
                o=None, lse=None, stream=None):
-    """O (bfloat16), LSE from e4m3 Q, K ([B, H, N, d]) and transposed V ([B, H, d, N])."""
+    """O (bfloat16), LSE from e4m3 Q, K ([B, H, N, d]) and transposed V ([B, H, d, vt_cols(N)])."""
     B, H, N, d = q8.shape
     if scale is None:
         scale = 1.0 / d ** 0.5
@@ -125,6 +145,14 @@ def fa_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, sca
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
     _check_dense(q8, k8, v8t, q_scale, k_scale, v_scale, o, lse)
+    _expect(q8, q8.shape, torch.uint8, "q8")
+    _expect(k8, q8.shape, torch.uint8, "k8")
+    _expect(v8t, (B, H, d, vt_cols(N)), torch.uint8, "v8t")
+    nt = (N + TILE_ROWS - 1) // TILE_ROWS
+    for t, name in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _expect(t, (B, H, nt), torch.float32, name)
+    _expect(o, (B, H, N, d), torch.bfloat16, "o")
+    _expect(lse, (B, H, N), torch.float32, "lse")
     lib = load_library()
     _check(lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), 1,
                           _ptr(o), _ptr(lse), B, H, N, d, int(causal), float(scale), _stream(stream)))

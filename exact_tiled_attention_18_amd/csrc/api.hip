@@ -20,7 +20,8 @@ int shape_status(int64_t B, int64_t H, int64_t N, int64_t d, int64_t* count) {
   if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
   int64_t bh, bhn, n;
   if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &n)) return FA_ERR_SHAPE;
-  if (N > INT32_MAX / 2) return FA_ERR_SHAPE;
+  // per-head byte offsets are 32-bit in the kernels: N * d * 4 (fp32) must fit
+  if (d > 0 && N > INT32_MAX / (4 * d)) return FA_ERR_SHAPE;
   // one launch: at most 2^24 workgroups of up to 256 threads
   if (bh > 0 && (N + 63) / 64 > (int64_t(1) << 24) / bh) return FA_ERR_SHAPE;
   *count = n;
@@ -86,9 +87,10 @@ int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t
   if (!x || !x8 || !x_scale) return FA_ERR_NULL;
   if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(x_scale, 4)) return FA_ERR_UNSUPPORTED;
   const int64_t sb = B * H * ((N + 127) / 128) * 4;
-  if (overlaps(x8, n, x, 2 * n) || overlaps(x_scale, sb, x, 2 * n) || overlaps(x8, n, x_scale, sb))
+  const int64_t xb = transpose_out ? B * H * d * FA_FP8_VT_COLS(N) : n;  // bytes of x8
+  if (overlaps(x8, xb, x, 2 * n) || overlaps(x_scale, sb, x, 2 * n) || overlaps(x8, xb, x_scale, sb))
     return FA_ERR_ALIAS;
-  if (signs && (overlaps(x8, n, signs, d) || overlaps(x_scale, sb, signs, d))) return FA_ERR_ALIAS;
+  if (signs && (overlaps(x8, xb, signs, d) || overlaps(x_scale, sb, signs, d))) return FA_ERR_ALIAS;
 
   const fa::QuantArgs a{x, x8, x_scale, signs, B, H, N, d, transpose_out, static_cast<hipStream_t>(stream)};
   return hip_status(fa::launch_quant_rotate_fp8(a));
@@ -109,9 +111,10 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const fl
     return FA_ERR_UNSUPPORTED;
   const int64_t ob = 2 * n, lb = B * H * N * 4, sb = B * H * ((N + 127) / 128) * 4;
   const void* ins[] = {q8, k8, v8};
+  const int64_t inb[] = {n, n, B * H * d * FA_FP8_VT_COLS(N)};
   const void* scs[] = {q_scale, k_scale, v_scale};
   for (int i = 0; i < 3; ++i)
-    if (overlaps(o, ob, ins[i], n) || overlaps(lse, lb, ins[i], n) || overlaps(o, ob, scs[i], sb) ||
+    if (overlaps(o, ob, ins[i], inb[i]) || overlaps(lse, lb, ins[i], inb[i]) || overlaps(o, ob, scs[i], sb) ||
         overlaps(lse, lb, scs[i], sb))
       return FA_ERR_ALIAS;
   if (overlaps(o, ob, lse, lb)) return FA_ERR_ALIAS;

@@ -1,39 +1,75 @@
 // FP8 (OCP e4m3) attention forward on gfx950 matrix cores
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales).
 //
-// Same structure as the bf16 kernel (query block per workgroup, key/value
-// tiles through LDS, online softmax with one final division, transposed
-// scores so that each lane owns a query), on operands produced by the
-// quantise+rotate pre-pass.  The FP8 variant of the pages doubles the matrix
-// throughput and relies on per-tile scales and the random rotation of Q and K
-// for accuracy (page "FlashAttention-Skalierung, Multi-GPU-Training und
-// Gewichtsquantisierung", section 1, FlashAttention-3 FP8 item).
+// The FP8 variant of the pages doubles the matrix throughput and keeps the
+// result accurate with per-tile scales and a random rotation of Q and K (page
+// "FlashAttention-Skalierung, Multi-GPU-Training und Gewichtsquantisierung",
+// section 1, FlashAttention-3 FP8 item).  Its operands come from the
+// quantise+rotate pre-pass: Q8, K8 as [B, H, N, 128] codes and V8 transposed
+// as [B, H, 128, N64] (rows padded with zero codes to a multiple of 64 keys),
+// each with one fp32 scale per 128-row tile.
 //
-// Scales.  A workgroup's 128 queries are exactly one quantisation tile of Q,
-// and a 64-key tile lies inside one 128-row tile of K and of V, so every
-// score of a (query tile, key tile) pair shares the factor
-// scale * q_scale * k_scale, folded into the softmax multiplier.  The
-// probabilities are multiplied by 256 and rounded to e4m3 for the second
-// product; the accumulator is kept in units of the current V tile's scale
-// (the correction factor of the online softmax also carries the ratio of
-// consecutive V scales), and the epilogue multiplies by the last V scale and
-// divides by 256 and by the row sum, which is accumulated from the unrounded
-// fp32 probabilities.
+// Structure (the bf16 kernel's, adapted to the fp8 instruction shape):
+//   * one workgroup per (256-query block, head, batch), 8 wavefronts of 32
+//     queries, heaviest causal blocks first;
+//   * 64-key tiles, the K extent of one P V matrix instruction; K8 and V8^T
+//     tiles go HBM -> registers (buffer loads, zero past the end) -> three
+//     rotating LDS slots, one step ahead;
+//   * scores transposed, S^T = K8 Q8^T, so a lane owns one query: for each
+//     32-key half of the tile the K rows are permuted (bits 2 and 3 of the
+//     row index swapped) and lane half g receives keys 8g..8g+7 and
+//     16+8g..16+8g+7;
+//   * the P V product contracts over the 64 keys in the order in which the
+//     probabilities already sit in the lanes (keys 8g, 16+8g, 32+8g, 48+8g,
+//     eight each): the V8^T tile is stored in LDS with its key columns in
+//     that order, so both operands of the product are read with two 16-byte
+//     LDS reads per lane and no data moves between lanes;
+//   * software pipeline: step t issues S_{t+1}, O += P_{t-1} V_{t-1} and the
+//     softmax of S_t in four chunks of one score and one output instruction
+//     each, with the vector work of the softmax between them.
+//
+// Scales.  Every score of a (query tile, key tile) pair shares the factor
+// scale * q_scale * k_scale, folded into the softmax multiplier.  V's tile
+// scale enters through the probabilities: with r = v_scale / v_scale_max
+// (v_scale_max: largest V scale of the head) written as r = 2^(e+1) * f,
+// f in [1/2, 1), the probabilities of the tile are multiplied by 2^6 * f
+// before rounding to e4m3 -- a shift of the exponent, at no cost -- and the
+// power of two 2^(e+1) goes exactly into the E8M0 block scale of the P
+// operand of the P V instruction.  The accumulator is then in units of
+// v_scale_max / 2^6 for every tile (no per-tile rescaling), and the rounding
+// of P keeps the same relative precision whatever V's scales are.  The
+// running row sum adds the probabilities times 2^6, so O = acc *
+// v_scale_max / sum and LSE follows from the same sum.  The softmax shift
+// moves lazily, only when a row maximum exceeds it by more than 2 (log2
+// units): probabilities stay below 4, so the rounded values stay below 256,
+// inside the e4m3 range (448).
+//
+// A negative scale flips the sign bit of every Q code (exact), a zero scale
+// zeroes Q; the kernel always works with a positive multiplier.
 #include "fa_device.h"
 #include "launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kBc = 64;
 constexpr int kD = 128;
-constexpr int kTile = 128;  // quantisation tile rows
-constexpr int kKS = kD + 16;   // K8 tile row stride (bytes)
-constexpr int kVS = kBc + 16;  // V8^T tile row stride (bytes)
+constexpr int kBc = 64;                 // keys per tile
+constexpr int kTile = 128;              // quantisation tile rows
+constexpr int kSlots = 3;               // LDS slots per operand
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBr = kWaves * 32;        // queries per workgroup
+constexpr int kKS = kD + 16;            // K8 tile row stride (bytes)
+constexpr int kVS = kBc + 16;           // V8^T tile row stride (bytes)
+constexpr int kKSlot = kBc * kKS;
+constexpr int kVSlot = kD * kVS;
+constexpr int kLdsBytes = kSlots * (kKSlot + kVSlot);
+constexpr float kSlack = 2.f;           // lazy shift slack (log2 units)
+constexpr float kPShift = 6.f;          // probabilities enter e4m3 times 2^6
+constexpr int NCH = 4;                  // chunks per step
+static_assert(kBc * kD / 16 == kThreads && kD * kBc / 16 == kThreads, "one 16-byte piece per thread");
 
 __device__ __forceinline__ int permuted_row(int i) { return i ^ ((((i >> 2) ^ (i >> 3)) & 1) * 0xC); }
-__device__ __forceinline__ int key_of_reg(int r, int g) { return (r & 7) + g * 8 + (r & 8) * 2; }
 
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -42,189 +78,365 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 }
 
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
-  // format 0 = fp8 e4m3 for both operands; block scales 127 = 2^0
+  // format 0 = e4m3 for both operands; block scales 127 = 2^0
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// the same with B scaled by 2^(bscale - 127) (E8M0 block scale, exact)
+__device__ __forceinline__ f32x16 mfma_fp8_bs(const i32x8& a, const i32x8& b, const f32x16& c, int bscale) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, bscale);
+}
+
+__device__ __forceinline__ i32x8 lds_read32(const char* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p), hi = *reinterpret_cast<const uint4*>(p + 16);
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// a wave-uniform value, kept in a scalar register
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+__device__ __forceinline__ float max_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(kWaves * 64) void attn_fwd_fp8_kernel(
+struct Attn8 {
+  // ---- per-thread state
+  i32x8 qf[2];          // Q8 as B operand, one per 64-column half of d
+  f32x16 oacc[4];       // O^T, 32 rows of d each
+  f32x16 sbuf[2][2];    // S^T of two consecutive tiles, two 32-key halves each
+  i32x8 pbuf[2];        // P8^T of two consecutive tiles
+  int pscale[2];        // their E8M0 block scales
+  i32x8 kop[2], vop[2]; // operand prefetch, by chunk parity
+  uint4 stg_k, stg_v;   // this thread's piece of the next K8 / V8^T tiles
+  float m, l, alpha, msub, rs;
+  float cst, inv_frac;  // softmax multiplier and 1 / f of the tile being softmaxed
+  int psc;               // its E8M0 scale 127 + e + 1
+  float cst_n, lf_n, inv_frac_n;  // the same for the next tile (lf = log2 f)
+  int psc_n;
+  float msub_q;
+
+  // ---- per-workgroup constants
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  char* kslot;
+  char* vslot;
+  const float* ks_head;
+  const float* vs_head;
+  int N, nTiles, qw0, lane, g, li;
+  int ldv;          // V8^T row length (keys, a multiple of 64)
+  int kst_off, vst_off;
+  int krd_off, vrd_off;
+  int vld_row;      // this thread's V8^T row (d) in a tile copy
+  int vld_col;      // ... and key offset inside the tile
+  float cq, log2_svmax, svmax;
+
+  __device__ __forceinline__ i32x8 read_k(int slot, int ch) const {
+    const int kb = ch & 1, kk = ch >> 1;
+    return lds_read32(kslot + slot * kKSlot + krd_off + kb * 32 * kKS + kk * 64);
+  }
+  __device__ __forceinline__ i32x8 read_v(int slot, int ch) const {
+    return lds_read32(vslot + slot * kVSlot + vrd_off + ch * 32 * kVS);
+  }
+  // this thread's 16-byte pieces of K8 tile t (row-major) and V8^T tile t (row d, 16 keys);
+  // buffer loads return zeros past the end of the head's data
+  __device__ __forceinline__ uint4 load_k(int t) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, t * kBc * kD + (int)threadIdx.x * 16, 0, 0));
+  }
+  __device__ __forceinline__ uint4 load_v(int t) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vld_row * ldv + t * kBc + vld_col, 0, 0));
+  }
+  __device__ __forceinline__ void store_k(int slot, const uint4& x) const {
+    *reinterpret_cast<uint4*>(kslot + slot * kKSlot + kst_off) = x;
+  }
+  __device__ __forceinline__ void store_v(int slot, const uint4& x) const {
+    // keys 16j..16j+7 and 16j+8..16j+15 of this row go to positions 8j and 32+8j
+    char* pv = vslot + slot * kVSlot + vst_off;
+    *reinterpret_cast<uint2*>(pv) = make_uint2(x.x, x.y);
+    *reinterpret_cast<uint2*>(pv + 32) = make_uint2(x.z, x.w);
+  }
+  // scale factors of key tile t (its 128-row quantisation tile), for its softmax one step later
+  __device__ __forceinline__ void load_scales(int t) {
+    const int j = min(t * kBc / kTile, nTiles - 1);
+    const float sk = ks_head[j], sv = vs_head[j];
+    cst_n = uniform(cq * sk);
+    const float lr = log2_fast(sv) - log2_svmax;          // log2(sv / svmax) <= 0
+    const float e = fmaxf(__builtin_floorf(lr), -120.f);  // E8M0 stays in range
+    lf_n = uniform(lr - e - 1.f);                         // log2 f, in [-1, 0) unless clamped
+    inv_frac_n = uniform(exp2_fast(-lf_n));
+    psc_n = __builtin_amdgcn_readfirstlane(128 + (int)e);
+  }
+
+  __device__ __forceinline__ void mask_scores(int B, int t) {
+    const int qi = qw0 + li;
+    const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - t * kBc - g * 8;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + (r & 7) + (r & 8) * 2 > lim) sbuf[B][kb][r] = -kInf;
+  }
+  __device__ __forceinline__ void softmax_slice(int ch, int B, int t, bool guard) {
+    if (ch == 0) {
+      cst = cst_n;
+      inv_frac = inv_frac_n;
+      psc = psc_n;
+      const float lf = lf_n;
+      if (guard) mask_scores(B, t);
+      const f32x16& s0 = sbuf[B][0];
+      const f32x16& s1 = sbuf[B][1];
+      float a[6];
+      a[0] = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
+      a[1] = fmaxf(fmaxf(s0[4], s0[5]), fmaxf(s0[6], s0[7]));
+      a[2] = fmaxf(fmaxf(s0[8], s0[9]), fmaxf(s0[10], s0[11]));
+      a[3] = fmaxf(fmaxf(s0[12], s0[13]), fmaxf(s0[14], s0[15]));
+      a[4] = fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]));
+      a[5] = fmaxf(fmaxf(s1[4], s1[5]), fmaxf(s1[6], s1[7]));
+      const float b0 = fmaxf(fmaxf(s1[8], s1[9]), fmaxf(s1[10], s1[11]));
+      const float b1 = fmaxf(fmaxf(s1[12], s1[13]), fmaxf(s1[14], s1[15]));
+      const float mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(b0, b1)));
+      const float mt = cst * max_pair(mx);  // -inf when no key of the tile is visible
+      const float m_new = mt > m + kSlack ? mt : m;
+      alpha = m_new == -kInf ? 1.f : exp2_fast(m - m_new);
+      m = m_new;
+      l *= alpha;
+      // 2^(cst*s - m + 6 + log2 f): the scaled probability that enters e4m3
+      msub_q = m_new == -kInf ? 0.f : m_new - kPShift - lf;
+      rs = 0.f;
+    } else if (ch == 1 || ch == 2) {
+      f32x16& s = sbuf[B][ch - 1];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = exp2_fast(fmaf(s[r], cst, -msub_q));
+      float h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = (s[i] + s[i + 4]) + (s[i + 8] + s[i + 12]);
+      rs += (h[0] + h[1]) + (h[2] + h[3]);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const f32x16& s = sbuf[B][kb];
+          const int b0 = 8 * hh;
+          pbuf[B][kb * 4 + hh * 2 + 0] = (int)pack_fp8x4(s[b0 + 0], s[b0 + 1], s[b0 + 2], s[b0 + 3]);
+          pbuf[B][kb * 4 + hh * 2 + 1] = (int)pack_fp8x4(s[b0 + 4], s[b0 + 5], s[b0 + 6], s[b0 + 7]);
+        }
+      pscale[B] = psc;
+      l += rs * inv_frac;
+    }
+  }
+
+  template <bool GUARD, int B>
+  __device__ __forceinline__ void step(int t, int sk_next, int sk_w, int sv_pv, int sv_next, int sv_w) {
+    f32x16(&snext)[2] = sbuf[B ^ 1];
+    const i32x8& pold = pbuf[B ^ 1];
+    const int psold = pscale[B ^ 1];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      if (ch + 1 < NCH) {
+        kop[(ch + 1) & 1] = read_k(sk_next, ch + 1);
+        vop[(ch + 1) & 1] = read_v(sv_pv, ch + 1);
+      } else {
+        kop[0] = read_k(sk_next == kSlots - 1 ? 0 : sk_next + 1, 0);
+        vop[0] = read_v(sv_next, 0);
+      }
+      {
+        const int kb = ch & 1, kk = ch >> 1;
+        if (kk == 0) {
+          const f32x16 z = {};
+          snext[kb] = mfma_fp8(kop[ch & 1], qf[0], z);
+        } else {
+          snext[kb] = mfma_fp8(kop[ch & 1], qf[1], snext[kb]);
+        }
+      }
+      oacc[ch] = mfma_fp8_bs(vop[ch & 1], pold, oacc[ch], psold);
+      softmax_slice(ch, B, t, GUARD);
+      if (ch == 1) {
+        store_k(sk_w, stg_k);
+        store_v(sv_w, stg_v);
+      }
+      if (ch == 2) {
+        stg_k = load_k(t + 4);
+        stg_v = load_v(t + 2);
+        load_scales(t + 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0); // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 200, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);  // DS writes
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // VMEM reads
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // deferred correction of O for rows whose shift moved
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    __syncthreads();
+  }
+
+  template <int B>
+  __device__ __forceinline__ void last_pv(int slot) {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const i32x8 a = ch == 0 ? vop[0] : read_v(slot, ch);
+      oacc[ch] = mfma_fp8_bs(a, pbuf[B], oacc[ch], pscale[B]);
+    }
+  }
+};
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
     const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vs,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int BH, int N, int nQB, float c) {
-  constexpr int BR = kWaves * 32;  // = kTile: one Q quantisation tile per workgroup
-  constexpr int KB = kBc / 32;
-  constexpr int DB = kD / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t ksm[kBc * kKS];
-  __shared__ __attribute__((aligned(16))) uint8_t vsm[kD * kVS];
-
+    uint16_t* __restrict__ o, float* __restrict__ lse, int BH, int N, int nQB, float c, uint32_t qxor,
+    uint32_t qand) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  Attn8<CAUSAL> s;
   const int L = blockIdx.x;
   const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
   const int bh = L % BH;
   const int nTiles = (N + kTile - 1) / kTile;
+  const int ldv = (N + kBc - 1) / kBc * kBc;
   const size_t base = (size_t)bh * N * kD;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, li = lane & 31;
-  const int q0 = qblk * BR;
-  const int qw0 = q0 + wave * 32;
-  const int qi = qw0 + li;
-  const float cq = c * qs[(size_t)bh * nTiles + qblk];
-  const bool cpos = c >= 0.f;
+  constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9-class GPUs
+  s.krs = __builtin_amdgcn_make_buffer_rsrc((void*)(k8 + base), (short)0, N * kD, kRsrcWord3);
+  s.vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v8t + (size_t)bh * kD * ldv), (short)0, kD * ldv, kRsrcWord3);
+  s.kslot = smem;
+  s.vslot = smem + kSlots * kKSlot;
+  s.ks_head = ks + (size_t)bh * nTiles;
+  s.vs_head = vs + (size_t)bh * nTiles;
+  s.N = N;
+  s.nTiles = nTiles;
+  s.ldv = ldv;
+  const int tid = threadIdx.x;
+  s.lane = tid & 63;
+  s.g = s.lane >> 5;
+  s.li = s.lane & 31;
+  {
+    const int krow = tid >> 3, kcol = (tid & 7) * 16;
+    s.kst_off = krow * kKS + kcol;
+    s.vld_row = tid >> 2;
+    s.vld_col = (tid & 3) * 16;
+    s.vst_off = s.vld_row * kVS + (tid & 3) * 8;
+    s.krd_off = permuted_row(s.li) * kKS + s.g * 32;
+    s.vrd_off = s.li * kVS + s.g * 32;
+  }
+  const int q0 = qblk * kBr;
+  s.qw0 = q0 + (tid >> 6) * 32;
+  const int qi = s.qw0 + s.li;
+  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
+  const int nT = (kv_end + kBc - 1) / kBc;
+  const int nFull = (CAUSAL ? min(N, q0 + 1) : N) / kBc;
 
-  // Q8 as B operand: per k-step of 64 columns, lane half g holds 32 consecutive columns
-  i32x8 qf[2];
+  // largest V scale of the head
+  {
+    float mx = 0.f;
+    for (int i = s.lane; i < nTiles; i += 64) mx = fmaxf(mx, s.vs_head[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    s.svmax = uniform(mx);
+    s.log2_svmax = uniform(log2_fast(mx));
+  }
+  s.cq = uniform(c * qs[(size_t)bh * nTiles + min(s.qw0 / kTile, nTiles - 1)]);
+
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
     if (qi < N) {
-      const uint8_t* p = q8 + base + (size_t)qi * kD + kk * 64 + g * 32;
+      const uint8_t* p = q8 + base + (size_t)qi * kD + kk * 64 + s.g * 32;
       lo = *reinterpret_cast<const uint4*>(p);
       hi = *reinterpret_cast<const uint4*>(p + 16);
     }
-    qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    lo = make_uint4((lo.x ^ qxor) & qand, (lo.y ^ qxor) & qand, (lo.z ^ qxor) & qand, (lo.w ^ qxor) & qand);
+    hi = make_uint4((hi.x ^ qxor) & qand, (hi.y ^ qxor) & qand, (hi.z ^ qxor) & qand, (hi.w ^ qxor) & qand);
+    s.qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
+  s.m = -kInf;
+  s.l = 0.f;
+  s.alpha = 1.f;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s.oacc[db][r] = 0.f;
 
-  f32x16 oacc[DB];
+  // ---- prologue: K_0..K_2 and V_0 into LDS, V slot 2 (standing for V_{-1}) and P_{-1}
+  // zero; S_0; stage K_3 and V_1; scales of tile 0; operands of step 0's first chunk
+  {
+    const uint4 k0 = s.load_k(0), k1 = s.load_k(1), k2 = s.load_k(2), v0 = s.load_v(0);
+    s.stg_k = s.load_k(3);
+    s.stg_v = s.load_v(1);
+    s.store_k(0, k0);
+    s.store_k(1, k1);
+    s.store_k(2, k2);
+    s.store_v(0, v0);
+    s.store_v(2, make_uint4(0, 0, 0, 0));
+  }
+  s.pbuf[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  s.pscale[1] = 127;
+  __syncthreads();
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m = -kInf, l = 0.f, sv_prev = 1.f;
+  for (int kb = 0; kb < 2; ++kb) {
+    const f32x16 z = {};
+    s.sbuf[0][kb] = mfma_fp8(s.read_k(0, kb), s.qf[0], z);
+    s.sbuf[0][kb] = mfma_fp8(s.read_k(0, kb + 2), s.qf[1], s.sbuf[0][kb]);
+  }
+  s.load_scales(0);
+  s.kop[0] = s.read_k(1, 0);
+  s.vop[0] = s.read_v(2, 0);
 
-  const int kv_end = CAUSAL ? min(N, q0 + BR) : N;
-  const int nT = (kv_end + kBc - 1) / kBc;
-  for (int t = 0; t < nT; ++t) {
-    const int k0 = t * kBc;
-    __syncthreads();
-    // K8 tile: 64 rows of 128 bytes
-#pragma unroll
-    for (int i = 0; i < kBc * kD / 16 / (kWaves * 64); ++i) {
-      const int cidx = tid + i * kWaves * 64;
-      const int row = cidx / (kD / 16), col = (cidx % (kD / 16)) * 16;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (k0 + row < N) val = *reinterpret_cast<const uint4*>(k8 + base + (size_t)(k0 + row) * kD + col);
-      *reinterpret_cast<uint4*>(&ksm[row * kKS + col]) = val;
-    }
-    // V8^T tile: 128 rows (d) of 64 key bytes, from the [d][N] layout
-    {
-      const uint8_t* vbase = v8t + (size_t)bh * kD * N;
-      if ((N & 15) == 0 && k0 + kBc <= N) {
-#pragma unroll
-        for (int i = 0; i < kD * kBc / 16 / (kWaves * 64); ++i) {
-          const int cidx = tid + i * kWaves * 64;
-          const int row = cidx / (kBc / 16), col = (cidx % (kBc / 16)) * 16;
-          *reinterpret_cast<uint4*>(&vsm[row * kVS + col]) =
-              *reinterpret_cast<const uint4*>(vbase + (size_t)row * N + k0 + col);
-        }
-      } else {
-        for (int i = tid; i < kD * kBc; i += kWaves * 64) {
-          const int row = i / kBc, col = i % kBc;
-          vsm[row * kVS + col] = (k0 + col < N) ? vbase[(size_t)row * N + k0 + col] : (uint8_t)0;
-        }
-      }
-    }
-    __syncthreads();
-    if (CAUSAL && k0 > qw0 + 31) continue;
-
-    const float cst = cq * ks[(size_t)bh * nTiles + k0 / kTile];
-    const float sv = vs[(size_t)bh * nTiles + k0 / kTile];
-
-    // S^T = K8 Q8^T
-    f32x16 s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int row = kb * 32 + permuted_row(li);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(&ksm[row * kKS + kk * 64 + g * 32]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&ksm[row * kKS + kk * 64 + g * 32 + 16]);
-        const i32x8 a = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        s[kb] = mfma_fp8(a, qf[kk], s[kb]);
-      }
-    }
-
-    const bool masked = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
-    float mx = cpos ? -kInf : kInf;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kb][r];
-        if (masked) {
-          const int key = k0 + kb * 32 + key_of_reg(r, g);
-          if (key >= N || (CAUSAL && key > qi)) x = cpos ? -kInf : kInf;
-        }
-        mx = cpos ? fmaxf(mx, x) : fminf(mx, x);
-      }
-    const float mo = xor32(mx);
-    mx = cpos ? fmaxf(mx, mo) : fminf(mx, mo);
-    const float mt = (mx == kInf || mx == -kInf) ? -kInf : cst * mx;
-    const float m_new = fmaxf(m, mt);
-    const float alpha = m_new == -kInf ? 1.f : exp2_fast(m - m_new);
-    const float msub = m_new == -kInf ? 0.f : m_new;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = exp2_fast(fmaf(s[kb][r], cst, -msub));
-        if (masked) {
-          const int key = k0 + kb * 32 + key_of_reg(r, g);
-          if (key >= N || (CAUSAL && key > qi)) p = 0.f;
-        }
-        s[kb][r] = p;
-        rs += p;
-      }
-    l = alpha * l + rs;
-    m = m_new;
-    const float fac = alpha * (sv_prev / sv);
-    sv_prev = sv;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= fac;
-
-    // P8^T as B operand: keys [8g, 8g+8), [16+8g, ...), [32+8g, ...), [48+8g, ...)
-    i32x8 pf;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int b0 = 8 * h;
-        pf[kb * 4 + h * 2 + 0] = (int)pack_fp8x4(s[kb][b0 + 0] * 256.f, s[kb][b0 + 1] * 256.f,
-                                                 s[kb][b0 + 2] * 256.f, s[kb][b0 + 3] * 256.f);
-        pf[kb * 4 + h * 2 + 1] = (int)pack_fp8x4(s[kb][b0 + 4] * 256.f, s[kb][b0 + 5] * 256.f,
-                                                 s[kb][b0 + 6] * 256.f, s[kb][b0 + 7] * 256.f);
-      }
-
-    // O^T += V8^T P8^T (accumulated in units of sv / 256)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint8_t* vr = &vsm[(db * 32 + li) * kVS + g * 8];
-      const uint2 a0 = *reinterpret_cast<const uint2*>(vr + 0);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 16);
-      const uint2 a2 = *reinterpret_cast<const uint2*>(vr + 32);
-      const uint2 a3 = *reinterpret_cast<const uint2*>(vr + 48);
-      const i32x8 a = {(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, (int)a3.x, (int)a3.y};
-      oacc[db] = mfma_fp8(a, pf, oacc[db]);
+  int sk_next = 1, sk_w = 0, sv_pv = 2, sv_next = 0, sv_w = 1;  // for t = 0
+  auto advance = [&]() {
+    sk_next = sk_next == 2 ? 0 : sk_next + 1;
+    sk_w = sk_w == 2 ? 0 : sk_w + 1;
+    sv_pv = sv_pv == 2 ? 0 : sv_pv + 1;
+    sv_next = sv_next == 2 ? 0 : sv_next + 1;
+    sv_w = sv_w == 2 ? 0 : sv_w + 1;
+  };
+  s.template step<true, 0>(0, sk_next, sk_w, sv_pv, sv_next, sv_w);
+  advance();
+  int t = 1;
+  for (; t + 1 < nFull; t += 2) {
+    s.template step<false, 1>(t, sk_next, sk_w, sv_pv, sv_next, sv_w);
+    advance();
+    s.template step<false, 0>(t + 1, sk_next, sk_w, sv_pv, sv_next, sv_w);
+    advance();
+  }
+  for (; t < nT; t += 2) {
+    s.template step<true, 1>(t, sk_next, sk_w, sv_pv, sv_next, sv_w);
+    advance();
+    if (t + 1 < nT) {
+      s.template step<true, 0>(t + 1, sk_next, sk_w, sv_pv, sv_next, sv_w);
+      advance();
     }
   }
+  if ((nT - 1) & 1) s.template last_pv<1>((nT - 1) % kSlots);
+  else s.template last_pv<0>((nT - 1) % kSlots);
 
-  const float lt = l + xor32(l);
+  // ---- epilogue: O = acc * svmax / sum, LSE = ln 2 * (m + log2(sum) - 6)
+  const float lt = sum_pair(s.l);
   if (qi < N) {
-    const float inv = sv_prev / (256.f * lt);
+    const float inv = s.svmax / lt;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const int dcol = db * 32 + 8 * a4 + 4 * g;
+        const int dcol = db * 32 + 8 * a4 + 4 * s.g;
         uint2 w;
-        w.x = pack_bf16x2(oacc[db][4 * a4 + 0] * inv, oacc[db][4 * a4 + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * a4 + 2] * inv, oacc[db][4 * a4 + 3] * inv);
+        w.x = pack_bf16x2(s.oacc[db][4 * a4 + 0] * inv, s.oacc[db][4 * a4 + 1] * inv);
+        w.y = pack_bf16x2(s.oacc[db][4 * a4 + 2] * inv, s.oacc[db][4 * a4 + 3] * inv);
         *reinterpret_cast<uint2*>(o + base + (size_t)qi * kD + dcol) = w;
       }
-    if (g == 0) lse[(size_t)bh * N + qi] = (m + log2_fast(lt)) * kLn2;
+    if (s.g == 0) lse[(size_t)bh * N + qi] = (s.m + log2_fast(lt) - kPShift) * kLn2;
   }
 }
 
@@ -232,15 +444,19 @@ __global__ __launch_bounds__(kWaves * 64) void attn_fwd_fp8_kernel(
 
 hipError_t launch_attn_fp8(const Fp8AttnArgs& a) {
   const int BH = (int)(a.B * a.H), N = (int)a.N;
-  const int nQB = (N + kTile - 1) / kTile;
-  const dim3 grid((unsigned)(nQB * BH)), block(kWaves * 64);
-  const float c = a.scale * kLog2e;
+  const int nQB = (N + kBr - 1) / kBr;
+  const dim3 grid((unsigned)(nQB * BH)), block(kThreads);
+  // positive multiplier: negate Q (flip every code's sign bit) for a negative scale,
+  // zero Q for a zero scale
+  const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
+  const uint32_t qxor = a.scale < 0.f ? 0x80808080u : 0u;
+  const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
   if (a.causal)
     hipLaunchKernelGGL((attn_fwd_fp8_kernel<true>), grid, block, 0, a.stream, a.q8, a.k8, a.v8t, a.q_scale,
-                       a.k_scale, a.v_scale, static_cast<uint16_t*>(a.o), a.lse, BH, N, nQB, c);
+                       a.k_scale, a.v_scale, static_cast<uint16_t*>(a.o), a.lse, BH, N, nQB, c, qxor, qand);
   else
     hipLaunchKernelGGL((attn_fwd_fp8_kernel<false>), grid, block, 0, a.stream, a.q8, a.k8, a.v8t, a.q_scale,
-                       a.k_scale, a.v_scale, static_cast<uint16_t*>(a.o), a.lse, BH, N, nQB, c);
+                       a.k_scale, a.v_scale, static_cast<uint16_t*>(a.o), a.lse, BH, N, nQB, c, qxor, qand);
   return hipGetLastError();
 }
 

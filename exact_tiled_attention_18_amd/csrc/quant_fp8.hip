@@ -16,8 +16,9 @@
 // One workgroup quantises one tile: it reads the tile once (bf16), keeps it
 // in registers through the transform and the amax reduction, and writes the
 // codes once -- the kernel moves each byte of HBM exactly once, which is its
-// bound.  For V the codes can be written transposed ([B, H, d, N]), so the
-// attention kernel's P V product reads keys contiguously.
+// bound.  For V the codes can be written transposed, [B, H, d, N64] with N64
+// = N rounded up to a multiple of 64 and zero codes in the padding, so the
+// attention kernel's P V product reads whole aligned 64-key rows.
 #include "fa_device.h"
 #include "launch.h"
 
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
     const int row = r0 + lrow;
     uint32_t c[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = e4m3_code(z[p][e] * mult);
+    for (int e = 0; e < 8; ++e) c[e] = row < N ? e4m3_code(z[p][e] * mult) : 0u;  // padding: code 0 (not -0)
     const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
     if constexpr (!TRANSPOSE) {
@@ -145,20 +146,15 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
   }
   if constexpr (TRANSPOSE) {
     __syncthreads();
-    // x8 is [B, H, D, N]: row `col` of this head holds the codes of all N rows
-    const int rows_here = min(kTileRows, N - r0);
-    uint8_t* dst = x8 + (size_t)bh * D * N + r0;
-    if ((N & 15) == 0 && rows_here == kTileRows) {
-      for (int i = tid; i < D * (kTileRows / 16); i += kThreads) {
-        const int col = i / (kTileRows / 16), ch = i % (kTileRows / 16);
-        *reinterpret_cast<uint4*>(dst + (size_t)col * N + ch * 16) =
-            *reinterpret_cast<const uint4*>(&tr[col * (kTileRows + 16) + ch * 16]);
-      }
-    } else {
-      for (int i = tid; i < D * kTileRows; i += kThreads) {
-        const int col = i / kTileRows, rr = i % kTileRows;
-        if (rr < rows_here) dst[(size_t)col * N + rr] = tr[col * (kTileRows + 16) + rr];
-      }
+    // x8 is [B, H, D, N64]: row `col` of this head holds the codes of all N rows,
+    // then code 0 up to N64
+    const int ldv = (N + 63) / 64 * 64;
+    const int chunks = min(kTileRows, ldv - r0) / 16;
+    uint8_t* dst = x8 + (size_t)bh * D * ldv + r0;
+    for (int i = tid; i < D * chunks; i += kThreads) {
+      const int col = i / chunks, ch = i % chunks;
+      *reinterpret_cast<uint4*>(dst + (size_t)col * ldv + ch * 16) =
+          *reinterpret_cast<const uint4*>(&tr[col * (kTileRows + 16) + ch * 16]);
     }
   }
 }

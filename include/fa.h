@@ -42,12 +42,16 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
+
+/* Row length (keys) of transposed V codes: N rounded up to a multiple of 64. */
+#define FA_FP8_VT_COLS(N) ((((N) + 63) / 64) * 64)
 
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                        */
-  FA_ERR_SHAPE = 2,       /* a negative size, or an element count beyond int64 */
+  FA_ERR_SHAPE = 2,       /* a negative size, an element count beyond int64,  */
+                          /* or N * d * 4 beyond INT32_MAX (per-head size)     */
   FA_ERR_UNSUPPORTED = 3, /* head dim, dtype, flag or layout not provided      */
   FA_ERR_SCALE = 4,       /* scale is NaN or infinite                          */
   FA_ERR_ALIAS = 5,       /* an output overlaps an input                       */
@@ -92,7 +96,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *             R = diag(signs) H_d / sqrt(d), H_d the Sylvester-ordered
  *             Hadamard matrix; Q and K must use the same signs.
  *   x8      : OCP e4m3 codes (uint8).  transpose_out = 0: [B, H, N, d];
- *             transpose_out = 1: [B, H, d, N] (the layout fa_fwd_fp8 wants for V).
+ *             transpose_out = 1: [B, H, d, FA_FP8_VT_COLS(N)], columns N and
+ *             beyond holding code 0 (the layout fa_fwd_fp8 wants for V).
  *   x_scale : float32 [B, H, ceil(N/128)]: one scale per tile of 128 rows
  *             (the last tile may be partial) = max |value| over the tile / 448,
  *             or 1 for an all-zero tile.  code = e4m3(value / scale), rounded
@@ -109,15 +114,17 @@ int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t
  * fa_fwd_fp8 -- attention forward on e4m3 operands with per-tile scales.
  *   q8, k8  : e4m3 codes [B, H, N, d] from fa_quant_rotate_fp8 with the same signs.
  *   v8      : e4m3 codes of V (not rotated); v_transposed must be 1 and v8
- *             laid out [B, H, d, N].
+ *             laid out [B, H, d, FA_FP8_VT_COLS(N)] with zero codes in the
+ *             padding columns, as fa_quant_rotate_fp8 writes it.
  *   q_scale, k_scale, v_scale : float32 [B, H, ceil(N/128)] tile scales.
  *   o       : bfloat16 [B, H, N, d];  lse: float32 [B, H, N].
  *   d       : 128.  causal: 0 or 1.  scale: finite.
  * Arithmetic: Q K^T and P V on fp8 MFMA with fp32 accumulation; the score of
  * a (query tile, key tile) pair is multiplied by scale * q_scale * k_scale;
- * probabilities are multiplied by 256 and rounded to e4m3 for the P V
- * product (the factor is divided out with V's tile scale); the row sums use
- * the unrounded fp32 probabilities.
+ * the probabilities of a key tile are multiplied by 2^6 * v_scale / (largest
+ * v_scale of the head) and rounded to e4m3 for the P V product (the factors
+ * are divided out at the end); the row sums use the unrounded fp32
+ * probabilities.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, v_transposed,
  * causal), FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP.
  */

@@ -70,7 +70,11 @@ def check_codes(codes_gpu, scale_gpu, x, signs, transposed=False):
     u = 2.0 ** -24
     codes_gpu = codes_gpu.cpu()
     if transposed:
-        codes_gpu = codes_gpu.transpose(-1, -2)
+        # [B, H, d, N64]: the rows past N are padding and must hold code 0
+        n = x.shape[-2]
+        assert codes_gpu.shape[-1] == (n + 63) // 64 * 64, codes_gpu.shape
+        assert int(codes_gpu[..., n:].abs().sum()) == 0 if codes_gpu.shape[-1] > n else True
+        codes_gpu = codes_gpu[..., :n].transpose(-1, -2)
     codes_gpu = codes_gpu.contiguous().numpy()
     sg = None if signs is None else np.asarray(signs.cpu() if hasattr(signs, "cpu") else signs)
     xf = to_np(x) if isinstance(x, torch.Tensor) else np.asarray(x, dtype=np.float64)
@@ -103,7 +107,7 @@ def fp8_errors(o_gpu, lse_gpu, q8, k8, v8t, qs, ks, vs, causal, scale, heads, ro
     """Errors of the fp8 kernel against the oracle of its own dequantised operands."""
     o_gpu, lse_gpu = to_np(o_gpu), to_np(lse_gpu)
     q8, k8 = q8.cpu().numpy(), k8.cpu().numpy()
-    v8 = v8t.cpu().transpose(-1, -2).contiguous().numpy()
+    v8 = v8t.cpu()[..., :q8.shape[-2]].transpose(-1, -2).contiguous().numpy()
     qs, ks, vs = qs.cpu().numpy(), ks.cpu().numpy(), vs.cpu().numpy()
     worst_rel = worst_abs = worst_lse = 0.0
     for b, h in heads:

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(fa):
 
 
 def test_version_and_status_strings(fa):
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     assert fa.fa_status_string(0) == "ok"
     assert fa.fa_status_string(3) == "unsupported argument"
     assert fa.fa_status_string(99) == "unknown status"
@@ -60,6 +60,9 @@ def test_fwd_validation(fa):
     assert _fwd(fa, B=-1) == fa.FA_ERR_SHAPE
     assert _fwd(fa, N=-5) == fa.FA_ERR_SHAPE
     assert _fwd(fa, B=1 << 40, H=1 << 30) == fa.FA_ERR_SHAPE  # element count overflows int64
+    # one head's fp32 bytes N * d * 4 must fit the kernels' 32-bit offsets
+    assert _fwd(fa, N=(2 ** 31 - 1) // (4 * 64) + 1) == fa.FA_ERR_SHAPE
+    assert fa.vt_cols(1) == 64 and fa.vt_cols(64) == 64 and fa.vt_cols(65) == 128
     assert _fwd(fa, d=96) == fa.FA_ERR_UNSUPPORTED
     assert _fwd(fa, dtype=7) == fa.FA_ERR_UNSUPPORTED
     assert _fwd(fa, causal=2) == fa.FA_ERR_UNSUPPORTED

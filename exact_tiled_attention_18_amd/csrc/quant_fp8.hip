@@ -11,7 +11,7 @@
 // fp32 registers; the 1/sqrt(d) factor is folded into the tile scale.  A tile
 // is 128 consecutive rows of one (batch, head) with all d columns; its scale
 // is amax / 448 and every value is divided by it and rounded to the nearest
-// e4m3 code (ties to even, saturating at +-448).
+// e4m3 code (ties to even; the largest magnitude maps to 448).
 //
 // One workgroup quantises one tile: it reads the tile once (bf16), keeps it
 // in registers through the transform and the amax reduction, and writes the
@@ -28,22 +28,38 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTileRows = 128;
 
-// fp32 -> OCP e4m3 code, round to nearest even, saturating at +-448, from the
-// format definition (bias 7, 3 mantissa bits, subnormal step 2^-9).
-__device__ __forceinline__ uint32_t e4m3_code(float t) {
-  const uint32_t u = __float_as_uint(t);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return 0x7Fu;  // NaN
-  const float af = __uint_as_float(a);
-  if (af < 0.015625f) {  // below 2^-6: subnormal grid m * 2^-9, m = 0..8
-    return sign | (uint32_t)__builtin_rintf(af * 512.0f);
+// four fp32 -> four OCP e4m3 codes packed in 32 bits (v_cvt_pk_fp8_f32: round to
+// nearest even).  The scaled values here satisfy |t| <= 448 up to one rounding
+// of the multiplier, far below 464, the first value that would not round to
+// the largest finite code 448.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// DPP move: `old` where the control's lane is invalid or the bank is masked off
+template <int CTRL, int BANK>
+__device__ __forceinline__ float dpp(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, 0xF, BANK, false));
+}
+// value held by the lane whose index differs in bit HM (HM = 1, 2, 4, 8; inside 16-lane rows)
+template <int HM>
+__device__ __forceinline__ float partner(float x) {
+  if constexpr (HM == 1) return dpp<0xB1, 0xF>(x, x);  // quad_perm [1, 0, 3, 2]
+  if constexpr (HM == 2) return dpp<0x4E, 0xF>(x, x);  // quad_perm [2, 3, 0, 1]
+  if constexpr (HM == 4) {
+    const float up = dpp<0x104, 0x5>(x, x);  // row_shl:4 into lanes 0-3 and 8-11 of each row
+    return dpp<0x114, 0xA>(up, x);           // row_shr:4 into lanes 4-7 and 12-15
   }
-  // keep 3 mantissa bits with round-to-nearest-even on the fp32 pattern,
-  // then move the exponent bias from 127 to 7
-  uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-  r -= (127u - 7u) << 3;
-  return sign | (r > 0x7Eu ? 0x7Eu : r);
+  return dpp<0x128, 0xF>(x, x);              // row_ror:8
+}
+
+template <int HM>
+__device__ __forceinline__ void butterfly(float (&z)[8], int cg) {
+  const float sgn = (cg & HM) ? -1.f : 1.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = fmaf(z[e], sgn, partner<HM>(z[e]));
 }
 
 template <int D, bool ROTATE, bool TRANSPOSE>
@@ -51,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ x8, float* __restrict__ x_scale,
     const int8_t* __restrict__ signs, int N, int nTiles) {
   constexpr int TPR = D / 8;                 // threads per row (8 values each)
+  static_assert(TPR == 8 || TPR == 16, "row groups of 8 or 16 lanes");
   constexpr int RPP = kThreads / TPR;        // rows per pass
   constexpr int PASSES = kTileRows / RPP;
   __shared__ float red[kThreads / 64];
@@ -96,16 +113,13 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
             z[p][e] = a + b;
             z[p][e + h] = a - b;
           }
-      // spans 8 .. D/2 pair this thread with the one whose column group differs in one bit
-#pragma unroll
-      for (int hm = 1; hm < TPR; hm <<= 1) {
-        const bool hi = (cg & hm) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float other = __shfl_xor(z[p][e], hm);
-          z[p][e] = hi ? (other - z[p][e]) : (z[p][e] + other);
-        }
-      }
+      // spans 8 .. D/2 pair this thread with the one whose column group differs in one
+      // bit (TPR consecutive lanes hold a row): (a, b) -> (a + b, a - b), the upper
+      // lane computing b * -1 + a exactly as a - b
+      butterfly<1>(z[p], cg);
+      butterfly<2>(z[p], cg);
+      butterfly<4>(z[p], cg);
+      if constexpr (TPR == 16) butterfly<8>(z[p], cg);
     }
   }
 
@@ -132,16 +146,17 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
   for (int p = 0; p < PASSES; ++p) {
     const int lrow = p * RPP + tid / TPR;
     const int row = r0 + lrow;
-    uint32_t c[8];
+    float t[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = row < N ? e4m3_code(z[p][e] * mult) : 0u;  // padding: code 0 (not -0)
-    const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    for (int e = 0; e < 8; ++e) t[e] = z[p][e] * mult;
+    // rows past N: code 0 (a sign flip of zero would otherwise give -0)
+    const uint32_t lo = row < N ? e4m3x4(t[0], t[1], t[2], t[3]) : 0u;
+    const uint32_t hi = row < N ? e4m3x4(t[4], t[5], t[6], t[7]) : 0u;
     if constexpr (!TRANSPOSE) {
       if (row < N) *reinterpret_cast<uint2*>(x8 + base + (size_t)row * D + cg * 8) = make_uint2(lo, hi);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tr[(cg * 8 + e) * (kTileRows + 16) + lrow] = (uint8_t)c[e];
+      for (int e = 0; e < 8; ++e) tr[(cg * 8 + e) * (kTileRows + 16) + lrow] = (uint8_t)((e < 4 ? lo : hi) >> (8 * (e & 3)));
     }
   }
   if constexpr (TRANSPOSE) {

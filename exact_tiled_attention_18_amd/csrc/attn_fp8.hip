@@ -118,12 +118,11 @@ struct Attn8 {
   float m, l, alpha, msub, rs;
   float cst, inv_frac;  // softmax multiplier and 1 / f of the tile being softmaxed
   int psc;               // its E8M0 scale 127 + e + 1
-  float cst_n, lf_n, inv_frac_n;  // the same for the next tile (lf = log2 f)
-  int psc_n;
+  float ks_n, vs_n;      // raw K and V tile scales of the next tile (loaded one step ahead)
   float msub_q;
 
   // ---- per-workgroup constants
-  __amdgpu_buffer_rsrc_t krs, vrs;
+  __amdgpu_buffer_rsrc_t krs, vrs, ksrs, vsrs;
   char* kslot;
   char* vslot;
   const float* ks_head;
@@ -160,16 +159,12 @@ struct Attn8 {
     *reinterpret_cast<uint2*>(pv) = make_uint2(x.x, x.y);
     *reinterpret_cast<uint2*>(pv + 32) = make_uint2(x.z, x.w);
   }
-  // scale factors of key tile t (its 128-row quantisation tile), for its softmax one step later
+  // K and V scales of key tile t (its 128-row quantisation tile), one step before its
+  // softmax; vector-memory loads, so waiting for them never waits for LDS traffic
   __device__ __forceinline__ void load_scales(int t) {
-    const int j = min(t * kBc / kTile, nTiles - 1);
-    const float sk = ks_head[j], sv = vs_head[j];
-    cst_n = uniform(cq * sk);
-    const float lr = log2_fast(sv) - log2_svmax;          // log2(sv / svmax) <= 0
-    const float e = fmaxf(__builtin_floorf(lr), -120.f);  // E8M0 stays in range
-    lf_n = uniform(lr - e - 1.f);                         // log2 f, in [-1, 0) unless clamped
-    inv_frac_n = uniform(exp2_fast(-lf_n));
-    psc_n = __builtin_amdgcn_readfirstlane(128 + (int)e);
+    const int off = min(t * kBc / kTile, nTiles - 1) * 4;
+    ks_n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ksrs, off, 0, 0));
+    vs_n = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vsrs, off, 0, 0));
   }
 
   __device__ __forceinline__ void mask_scores(int B, int t) {
@@ -183,23 +178,27 @@ struct Attn8 {
   }
   __device__ __forceinline__ void softmax_slice(int ch, int B, int t, bool guard) {
     if (ch == 0) {
-      cst = cst_n;
-      inv_frac = inv_frac_n;
-      psc = psc_n;
-      const float lf = lf_n;
+      // this tile's factors: multiplier, r = sv / svmax = 2^(e+1) f, 1 / f, E8M0 scale
+      cst = uniform(cq * ks_n);
+      const float lr = log2_fast(vs_n) - log2_svmax;        // log2 r <= 0
+      const float e = fmaxf(__builtin_floorf(lr), -120.f);  // E8M0 stays in range
+      const float lf = uniform(lr - e - 1.f);               // log2 f, in [-1, 0) unless clamped
+      inv_frac = uniform(exp2_fast(-lf));
+      psc = __builtin_amdgcn_readfirstlane(128 + (int)e);
       if (guard) mask_scores(B, t);
       const f32x16& s0 = sbuf[B][0];
       const f32x16& s1 = sbuf[B][1];
-      float a[6];
-      a[0] = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
-      a[1] = fmaxf(fmaxf(s0[4], s0[5]), fmaxf(s0[6], s0[7]));
-      a[2] = fmaxf(fmaxf(s0[8], s0[9]), fmaxf(s0[10], s0[11]));
-      a[3] = fmaxf(fmaxf(s0[12], s0[13]), fmaxf(s0[14], s0[15]));
-      a[4] = fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]));
-      a[5] = fmaxf(fmaxf(s1[4], s1[5]), fmaxf(s1[6], s1[7]));
-      const float b0 = fmaxf(fmaxf(s1[8], s1[9]), fmaxf(s1[10], s1[11]));
-      const float b1 = fmaxf(fmaxf(s1[12], s1[13]), fmaxf(s1[14], s1[15]));
-      const float mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(b0, b1)));
+      // row maximum over the 32 scores: a tree of three-input maxima
+      float a[11];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) a[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
+      a[5] = fmaxf(fmaxf(s0[15], s1[0]), s1[1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[6 + i] = fmaxf(fmaxf(s1[2 + 3 * i], s1[3 + 3 * i]), s1[4 + 3 * i]);
+      a[10] = fmaxf(s1[14], s1[15]);
+      const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
+      const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]), b3 = fmaxf(a[9], a[10]);
+      const float mx = fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
       const float mt = cst * max_pair(mx);  // -inf when no key of the tile is visible
       const float m_new = mt > m + kSlack ? mt : m;
       alpha = m_new == -kInf ? 1.f : exp2_fast(m - m_new);
@@ -261,9 +260,9 @@ struct Attn8 {
         store_v(sv_w, stg_v);
       }
       if (ch == 2) {
+        load_scales(t + 1);
         stg_k = load_k(t + 4);
         stg_v = load_v(t + 2);
-        load_scales(t + 1);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -315,6 +314,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   s.vslot = smem + kSlots * kKSlot;
   s.ks_head = ks + (size_t)bh * nTiles;
   s.vs_head = vs + (size_t)bh * nTiles;
+  s.ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)s.ks_head, (short)0, nTiles * 4, kRsrcWord3);
+  s.vsrs = __builtin_amdgcn_make_buffer_rsrc((void*)s.vs_head, (short)0, nTiles * 4, kRsrcWord3);
   s.N = N;
   s.nTiles = nTiles;
   s.ldv = ldv;

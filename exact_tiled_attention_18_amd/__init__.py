@@ -55,6 +55,10 @@ def load_library():
     lib.fa_quant_rotate_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.fa_fwd_fp8.restype = i32
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, f32, vp]
+    lib.fa_fwd_partial.restype = i32
+    lib.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
+    lib.fa_merge.restype = i32
+    lib.fa_merge.argtypes = [vp, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp]
     _lib = lib
     return lib
 
@@ -168,3 +172,65 @@ def fp8_attention(q, k, v, signs, causal: bool = False, scale: float | None = No
     v8t, vs = fa_quant_rotate_fp8(v, None, True, stream=stream)
     o, lse = fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale, stream=stream)
     return o, lse, (q8, k8, v8t, qs, ks, vs)
+
+
+def fa_fwd_partial(q, k, v, q_pos0: int, k_begin: int, k_end: int, causal: bool = False,
+                   scale: float | None = None, o_part=None, lse_part=None, stream=None):
+    """O (float32, normalised over the range) and LSE of bfloat16 queries q [B, H, Nq, d]
+    (query i at key position q_pos0 + i) against keys k_begin <= j < k_end of k, v [B, H, Nk, d]."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    if o_part is None:
+        o_part = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_dense(q, k, v, o_part, lse_part)
+    _expect(q, (B, H, Nq, d), torch.bfloat16, "q")
+    _expect(k, (B, H, Nk, d), torch.bfloat16, "k")
+    _expect(v, (B, H, Nk, d), torch.bfloat16, "v")
+    _expect(o_part, (B, H, Nq, d), torch.float32, "o_part")
+    _expect(lse_part, (B, H, Nq), torch.float32, "lse_part")
+    lib = load_library()
+    _check(lib.fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, H, Nq, Nk, d,
+                              int(q_pos0), int(k_begin), int(k_end), int(causal), float(scale), FA_BF16,
+                              _stream(stream)))
+    return o_part, lse_part
+
+
+def fa_merge(o_parts, lse_parts, dtype=torch.bfloat16, o=None, lse=None, stream=None):
+    """O [B, H, N, d] (dtype) and LSE [B, H, N] over the union of the key ranges of
+    o_parts (float32 [n, B, H, N, d]) and lse_parts (float32 [n, B, H, N])."""
+    n, B, H, N, d = o_parts.shape
+    code = {torch.float32: FA_F32, torch.bfloat16: FA_BF16}.get(dtype, -1)
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    _check_dense(o_parts, lse_parts, o, lse)
+    _expect(lse_parts, (n, B, H, N), torch.float32, "lse_parts")
+    _expect(o_parts, (n, B, H, N, d), torch.float32, "o_parts")
+    _expect(o, (B, H, N, d), dtype, "o")
+    _expect(lse, (B, H, N), torch.float32, "lse")
+    lib = load_library()
+    _check(lib.fa_merge(_ptr(o_parts), _ptr(lse_parts), n, _ptr(o), _ptr(lse), B, H, N, d, code, _stream(stream)))
+    return o, lse
+
+
+def split_kv_attention(q, k, v, n_splits: int, causal: bool = False, scale: float | None = None,
+                       q_pos0: int | None = None, stream=None):
+    """Split-KV forward: the keys [0, Nk) cut into n_splits contiguous ranges, one
+    fa_fwd_partial call per range into one buffer, then fa_merge.  By default the
+    queries are the last Nq positions of the key sequence (q_pos0 = Nk - Nq)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if q_pos0 is None:
+        q_pos0 = Nk - Nq
+    o_parts = torch.empty((n_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    lse_parts = torch.empty((n_splits, B, H, Nq), dtype=torch.float32, device=q.device)
+    bounds = [Nk * i // n_splits for i in range(n_splits + 1)]
+    for i in range(n_splits):
+        fa_fwd_partial(q, k, v, q_pos0, bounds[i], bounds[i + 1], causal, scale, o_part=o_parts[i],
+                       lse_part=lse_parts[i], stream=stream)
+    return fa_merge(o_parts, lse_parts, q.dtype, stream=stream)

@@ -66,6 +66,10 @@
 #include "fa_device.h"
 #include "launch.h"
 
+#ifndef FA_BF16_QB
+#define FA_BF16_QB 1
+#endif
+
 namespace fa {
 namespace {
 
@@ -130,7 +134,9 @@ struct Attn {
   __amdgpu_buffer_rsrc_t krs, vrs;  // this head's K and V; reads past N return zeros
   char* kslot;
   char* vslot;
-  int N, qw0, lane, g, li;
+  int kn;    // keys used: rows k0 .. k0 + kn - 1 of this head's K and V
+  int qpos;  // position of query 0 relative to key k0 (causal: query i sees keys j <= qpos + i)
+  int qw0, lane, g, li;
   int ld_off;   // byte offset of this thread's first 16-byte piece inside a tile
   int kst_off;  // LDS byte offset of that piece in a K slot
   int vst_off;  // ... in a V slot
@@ -174,11 +180,11 @@ struct Attn {
   // the row maximum of c*s is c*max(s) and -inf marks a masked score.
   __device__ __forceinline__ void mask_scores(int B, int t) {
     // register r of lane half g holds key t*kBc + (r & 7) + 8*g + 2*(r & 8),
-    // visible to query qi iff that key <= min(qi, N - 1)
+    // visible to query qi iff that key < kn and (causal) <= qpos + qi
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const int qi = qw0 + qb * 32 + li;
-      const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - t * kBc - g * 8;
+      const int lim = (CAUSAL ? min(qpos + qi, kn - 1) : kn - 1) - t * kBc - g * 8;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if ((r & 7) + (r & 8) * 2 > lim) sbuf[B][qb][r] = -kInf;
@@ -338,10 +344,19 @@ struct Attn {
   }
 };
 
-template <int D, bool CAUSAL, int QB>
+// Rows of one launch: queries 0 .. nq-1 of each head against keys k0 .. k0+kn-1 of
+// its nk rows of K and V; query i sits at key position qpos + i (relative to k0).
+// The plain forward has nq = nk = kn = N, k0 = qpos = 0.
+struct Geom {
+  int nq, nk, k0, kn, qpos;
+};
+
+// PART: partial result over a key range -- O in fp32 (normalised over the range)
+// and rows that see no key written as O = 0, LSE = -inf.
+template <int D, bool CAUSAL, int QB, bool PART>
 __global__ __launch_bounds__(QB == 1 ? 512 : 256) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int BH, int N, int nQB, float c, uint32_t qxor,
+    void* __restrict__ o, float* __restrict__ lse, int BH, Geom gm, int nQB, float c, uint32_t qxor,
     uint32_t qand) {
   using A = Attn<D, CAUSAL, QB>;
   using Ly = typename A::Ly;
@@ -355,13 +370,16 @@ __global__ __launch_bounds__(QB == 1 ? 512 : 256) void attn_fwd_bf16_kernel(
   const int L = blockIdx.x;
   const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
   const int bh = L % BH;
+  const int N = gm.nq;  // query rows
   const size_t base = (size_t)bh * N * D;
+  const size_t kbase = ((size_t)bh * gm.nk + gm.k0) * D;
   constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9-class GPUs
-  s.krs = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, N * D * 2, kRsrcWord3);
-  s.vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, N * D * 2, kRsrcWord3);
+  s.krs = __builtin_amdgcn_make_buffer_rsrc((void*)(k + kbase), (short)0, gm.kn * D * 2, kRsrcWord3);
+  s.vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v + kbase), (short)0, gm.kn * D * 2, kRsrcWord3);
   s.kslot = smem;
   s.vslot = smem + kSlots * Ly::KSLOT;
-  s.N = N;
+  s.kn = gm.kn;
+  s.qpos = gm.qpos;
   const int tid = threadIdx.x;
   s.lane = tid & 63;
   s.g = s.lane >> 5;
@@ -379,10 +397,26 @@ __global__ __launch_bounds__(QB == 1 ? 512 : 256) void attn_fwd_bf16_kernel(
   const int q0 = qblk * kBr;
   s.qw0 = q0 + (tid >> 6) * kW;
   s.c = c;
-  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
-  const int nT = (kv_end + kBc - 1) / kBc;
+  const int kv_end = CAUSAL ? min(gm.kn, gm.qpos + q0 + kBr) : gm.kn;
+  const int nT = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
   // tiles 0 .. nFull-1 hold only keys that every query of the workgroup sees
-  const int nFull = (CAUSAL ? min(N, q0 + 1) : N) / kBc;
+  const int nFull = max(0, CAUSAL ? min(gm.kn, gm.qpos + q0 + 1) : gm.kn) / kBc;
+  if (PART && nT == 0) {  // no key visible to any query of the block (uniform: before any barrier)
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int qi = s.qw0 + qb * 32 + s.li;
+      if (qi < N) {
+        float* op = static_cast<float*>(o) + base + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4)
+            *reinterpret_cast<float4*>(op + db * 32 + 8 * a4 + 4 * s.g) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (s.g == 0) lse[(size_t)bh * N + qi] = -kInf;
+      }
+    }
+    return;
+  }
 
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -479,50 +513,70 @@ __global__ __launch_bounds__(QB == 1 ? 512 : 256) void attn_fwd_bf16_kernel(
     const float lht = s.lh[qb] + xor32(s.lh[qb]);
     const int qi = s.qw0 + qb * 32 + s.li;
     if (qi < N) {
-      const float inv = 1.f / lht;
+      if constexpr (PART) {
+        // a row with no visible key in the range has l = 0: O = 0, LSE = -inf
+        const float inv = lht > 0.f ? 1.f / lht : 0.f;
+        float* op = static_cast<float*>(o) + base + (size_t)qi * D;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int dcol = db * 32 + 8 * a4 + 4 * s.g;
-          uint2 wv;
-          wv.x = pack_bf16x2(s.oacc[db][qb][4 * a4 + 0] * inv, s.oacc[db][qb][4 * a4 + 1] * inv);
-          wv.y = pack_bf16x2(s.oacc[db][qb][4 * a4 + 2] * inv, s.oacc[db][qb][4 * a4 + 3] * inv);
-          *reinterpret_cast<uint2*>(o + base + (size_t)qi * D + dcol) = wv;
-        }
-      if (s.g == 0) lse[(size_t)bh * N + qi] = (s.m[qb] + log2_fast(lt)) * kLn2;
+          for (int a4 = 0; a4 < 4; ++a4)
+            *reinterpret_cast<float4*>(op + db * 32 + 8 * a4 + 4 * s.g) =
+                make_float4(s.oacc[db][qb][4 * a4 + 0] * inv, s.oacc[db][qb][4 * a4 + 1] * inv,
+                            s.oacc[db][qb][4 * a4 + 2] * inv, s.oacc[db][qb][4 * a4 + 3] * inv);
+        if (s.g == 0) lse[(size_t)bh * N + qi] = lt > 0.f ? (s.m[qb] + log2_fast(lt)) * kLn2 : -kInf;
+      } else {
+        const float inv = 1.f / lht;
+        uint16_t* op = static_cast<uint16_t*>(o) + base + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            uint2 wv;
+            wv.x = pack_bf16x2(s.oacc[db][qb][4 * a4 + 0] * inv, s.oacc[db][qb][4 * a4 + 1] * inv);
+            wv.y = pack_bf16x2(s.oacc[db][qb][4 * a4 + 2] * inv, s.oacc[db][qb][4 * a4 + 3] * inv);
+            *reinterpret_cast<uint2*>(op + db * 32 + 8 * a4 + 4 * s.g) = wv;
+          }
+        if (s.g == 0) lse[(size_t)bh * N + qi] = (s.m[qb] + log2_fast(lt)) * kLn2;
+      }
     }
   }
 }
 
-template <int D, bool CAUSAL, int QB>
-hipError_t launch(const AttnArgs& a) {
+template <int D, bool CAUSAL, int QB, bool PART>
+hipError_t launch(const AttnArgs& a, const Geom& gm) {
   constexpr int kBr = Attn<D, CAUSAL, QB>::kBr;
   constexpr int kThreads = Attn<D, CAUSAL, QB>::kThreads;
-  const int BH = (int)(a.B * a.H), N = (int)a.N;
-  const int nQB = (N + kBr - 1) / kBr;
+  const int BH = (int)(a.B * a.H);
+  const int nQB = (gm.nq + kBr - 1) / kBr;
   // the kernel needs a positive multiplier c: scale * (q . k) = |scale| * ((-q) . k) for
   // scale < 0 (negating bf16 is exact), and a zero scale is the same as zero queries
   const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
   const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB>), dim3((unsigned)(nQB * BH)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB, PART>), dim3((unsigned)(nQB * BH)), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, BH, N, nQB, c,
-                     qxor, qand);
+                     static_cast<const uint16_t*>(a.v), a.o, a.lse, BH, gm, nQB, c, qxor, qand);
   return hipGetLastError();
+}
+
+template <bool PART>
+hipError_t dispatch(const AttnArgs& a, const Geom& gm) {
+  constexpr int QB = FA_BF16_QB;
+  if (a.d == 64) return a.causal ? launch<64, true, QB, PART>(a, gm) : launch<64, false, QB, PART>(a, gm);
+  return a.causal ? launch<128, true, QB, PART>(a, gm) : launch<128, false, QB, PART>(a, gm);
 }
 
 }  // namespace
 
-#ifndef FA_BF16_QB
-#define FA_BF16_QB 1
-#endif
-
 hipError_t launch_attn_bf16(const AttnArgs& a) {
-  constexpr int QB = FA_BF16_QB;
-  if (a.d == 64) return a.causal ? launch<64, true, QB>(a) : launch<64, false, QB>(a);
-  return a.causal ? launch<128, true, QB>(a) : launch<128, false, QB>(a);
+  const int n = (int)a.N;
+  return dispatch<false>(a, Geom{n, n, 0, n, 0});
+}
+
+hipError_t launch_attn_bf16_partial(const AttnArgs& a, const PartialArgs& p) {
+  const Geom gm{(int)a.N, (int)p.nk, (int)p.k_begin, (int)(p.k_end - p.k_begin), (int)(p.q_pos0 - p.k_begin)};
+  return dispatch<true>(a, gm);
 }
 
 }  // namespace fa

@@ -23,6 +23,28 @@ struct AttnArgs {
 hipError_t launch_attn_f32(const AttnArgs& a);
 hipError_t launch_attn_bf16(const AttnArgs& a);
 
+// Partial forward over a key range (AttnArgs.N = query rows, AttnArgs.o = float32 O).
+struct PartialArgs {
+  int64_t nk;       // key rows per head in k and v
+  int64_t q_pos0;   // key position of query 0
+  int64_t k_begin;  // first key used
+  int64_t k_end;    // one past the last key used
+};
+hipError_t launch_attn_bf16_partial(const AttnArgs& a, const PartialArgs& p);
+
+// O, LSE of the union of key ranges from n partial results.
+struct MergeArgs {
+  const float* o_parts;    // [n, B, H, N, d]
+  const float* lse_parts;  // [n, B, H, N]
+  int64_t n;
+  void* o;                 // [B, H, N, d] of dtype
+  float* lse;              // [B, H, N]
+  int64_t B, H, N, d;
+  int dtype;               // FA_F32 or FA_BF16
+  hipStream_t stream;
+};
+hipError_t launch_merge(const MergeArgs& a);
+
 struct QuantArgs {
   const void* x;
   uint8_t* x8;

@@ -1,0 +1,86 @@
+// Merge of partial attention results over disjoint key ranges.
+//
+// A row's softmax over a union of key ranges follows from the ranges' own
+// results, because the exponentials add: with L_s the logsumexp of range s and
+// O_s its normalised output, the union has L = log(sum_s exp(L_s)) and
+// O = sum_s exp(L_s - L) O_s.  This is the rescaling identity behind the
+// pages' online softmax (FlashAttention-2 wiki page, "Technische Architektur",
+// item 1; page "FlashAttention-Skalierung, Multi-GPU-Training und
+// Gewichtsquantisierung", section 1) applied once to whole blocks: the step
+// that lets one row be split over key ranges (split-KV) or over devices.
+//
+// One wavefront per row; the kernel reads each partial once and writes O and
+// LSE once -- it is bound by HBM.  Ranges in which a row sees no key carry
+// L_s = -inf and contribute nothing; a row that sees no key at all gets
+// O = 0, L = -inf.
+#include "fa_device.h"
+#include "launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // wavefronts per workgroup
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(kRowsPerBlock * 64) void merge_kernel(const float* __restrict__ o_parts,
+                                                                   const float* __restrict__ lse_parts, int n,
+                                                                   void* __restrict__ o, float* __restrict__ lse,
+                                                                   int64_t rows) {
+  constexpr int C = D / 64;  // columns per lane
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  float mx = -kInf;
+  for (int s = 0; s < n; ++s) mx = fmaxf(mx, lse_parts[(int64_t)s * rows + row]);
+  float acc[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) acc[j] = 0.f;
+  float sum = 0.f;
+  if (mx != -kInf) {
+    for (int s = 0; s < n; ++s) {
+      const float w = exp2_fast((lse_parts[(int64_t)s * rows + row] - mx) * kLog2e);  // exp(-inf) = 0
+      sum += w;
+      const float* src = o_parts + ((int64_t)s * rows + row) * D + lane * C;
+      if constexpr (C == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(src);
+        acc[0] = fmaf(w, x.x, acc[0]);
+        acc[1] = fmaf(w, x.y, acc[1]);
+      } else {
+        acc[0] = fmaf(w, src[0], acc[0]);
+      }
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  if constexpr (BF16) {
+    uint16_t* dst = static_cast<uint16_t*>(o) + row * D + lane * C;
+    if constexpr (C == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      dst[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xFFFFu);
+    }
+  } else {
+    float* dst = static_cast<float*>(o) + row * D + lane * C;
+#pragma unroll
+    for (int j = 0; j < C; ++j) dst[j] = acc[j] * inv;
+  }
+  if (lane == 0) lse[row] = sum > 0.f ? mx + log2_fast(sum) * kLn2 : -kInf;
+}
+
+template <int D>
+hipError_t launch_d(const MergeArgs& a) {
+  const int64_t rows = a.B * a.H * a.N;
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(kRowsPerBlock * 64);
+  if (a.dtype == 1)
+    hipLaunchKernelGGL((merge_kernel<D, true>), grid, block, 0, a.stream, a.o_parts, a.lse_parts, (int)a.n, a.o,
+                       a.lse, rows);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, false>), grid, block, 0, a.stream, a.o_parts, a.lse_parts, (int)a.n, a.o,
+                       a.lse, rows);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a) { return a.d == 64 ? launch_d<64>(a) : launch_d<128>(a); }
+
+}  // namespace fa

@@ -133,6 +133,47 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                int v_transposed, void* o, float* lse, int64_t B, int64_t H, int64_t N,
                int64_t d, int causal, float scale, void* stream);
 
+/*
+ * fa_fwd_partial -- attention of queries against one range of keys: the
+ * building block of a split-KV forward and of merging results computed apart
+ * (on other streams or devices).  The softmax of a row over a union of key
+ * ranges follows exactly from the ranges' own outputs and logsumexps
+ * (fa_merge), by the same rescaling that the online softmax applies tile by
+ * tile (page "FlashAttention-Skalierung, Multi-GPU-Training und
+ * Gewichtsquantisierung", section 1; FlashAttention-2 wiki page,
+ * "Technische Architektur", item 1).
+ *   q        : bfloat16 [B, H, Nq, d]; query i sits at key position q_pos0 + i.
+ *   k, v     : bfloat16 [B, H, Nk, d]; keys k_begin <= j < k_end are used
+ *              (and, when causal, only j <= q_pos0 + i).
+ *   o_part   : float32 [B, H, Nq, d]: O normalised over the visible keys of the
+ *              range; 0 for a row that sees none of them.
+ *   lse_part : float32 [B, H, Nq]: natural logsumexp of the scaled visible
+ *              scores; -inf for a row that sees none of them.
+ *   d        : 64 or 128.  dtype: FA_BF16.  causal: 0 or 1.  scale: finite.
+ *   0 <= k_begin <= k_end <= Nk;  0 <= q_pos0 <= INT32_MAX / 2 - Nq.
+ * fa_fwd(q, k, v) with Nq = Nk = N equals this call with q_pos0 = 0 and the
+ * range [0, N), up to the precision of O (fp32 here, bf16 there).
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, dtype, causal),
+ * FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP.
+ */
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t q_pos0,
+                   int64_t k_begin, int64_t k_end, int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_merge -- O and LSE over the union of n_parts disjoint key ranges from
+ * their partial results: LSE = log(sum_s exp(LSE_s)), O = sum_s exp(LSE_s - LSE) O_s.
+ *   o_parts   : float32 [n_parts, B, H, N, d];  lse_parts: float32 [n_parts, B, H, N]
+ *               (as written by fa_fwd_partial; -inf marks a range a row does not see).
+ *   o         : [B, H, N, d] of dtype (FA_F32 or FA_BF16);  lse: float32 [B, H, N].
+ *   A row that sees no key in any range gets O = 0 and LSE = -inf.
+ *   d         : 64 or 128.  n_parts >= 1.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, dtype),
+ * FA_ERR_ALIAS, FA_ERR_HIP.
+ */
+int fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -138,3 +138,54 @@ def bruteforce(q, k, v, causal: bool, scale: float):
                     o[b, h, i, c] = math.fsum(w[j] * v[b, h, j, c] for j in visible) / z
                 lse[b, h, i] = m + math.log(z)
     return o, lse
+
+
+def partial(q, k, v, causal: bool, scale: float, q_pos0: int, k_begin: int, k_end: int):
+    """Attention of queries against one range of keys, for [B, H, Nq, d] queries and
+    [B, H, Nk, d] keys and values.
+
+    Query i sits at key position q_pos0 + i; it sees keys k_begin <= j < k_end and,
+    when causal, only j <= q_pos0 + i.  Returns (O, LSE), float64 [B, H, Nq, d] and
+    [B, H, Nq], with O normalised over the visible keys; a row that sees no key of
+    the range gets O = 0 and LSE = -inf (the empty sum).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    B, H, Nq, _ = q.shape
+    pos = q_pos0 + np.arange(Nq)
+    keys = np.arange(k_begin, k_end)
+    o = np.zeros((B, H, Nq, v.shape[-1]))
+    lse = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h, k_begin:k_end].T)
+            if causal:
+                s[keys[None, :] > pos[:, None]] = -np.inf
+            seen = np.isfinite(s).any(axis=1)
+            if not seen.any():
+                continue
+            s, vv = s[seen], v[b, h, k_begin:k_end]
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)
+            o[b, h, seen] = (e / l) @ vv
+            lse[b, h, seen] = m[:, 0] + np.log(l[:, 0])
+    return o, lse
+
+
+def merge(o_parts, lse_parts):
+    """O and LSE over the union of disjoint key ranges from their partial results.
+
+    The exponentials of the ranges add: LSE = log sum_s exp(LSE_s), and
+    O = sum_s exp(LSE_s - LSE) O_s (the rescaling the online softmax applies per
+    tile, here once per range).  Ranges with LSE_s = -inf contribute nothing; a row
+    with every LSE_s = -inf gets O = 0, LSE = -inf.
+    o_parts: [n, ..., d];  lse_parts: [n, ...].
+    """
+    o_parts, lse_parts = _as_f64(o_parts), _as_f64(lse_parts)
+    m = lse_parts.max(axis=0)
+    alive = np.isfinite(m)
+    w = np.where(alive[None], np.exp(lse_parts - np.where(alive, m, 0.0)[None]), 0.0)
+    z = w.sum(axis=0)
+    lse = np.where(alive, np.where(alive, m, 0.0) + np.log(np.where(alive, z, 1.0)), -np.inf)
+    o = np.where(alive[..., None], (w[..., None] * o_parts).sum(axis=0) / np.where(alive, z, 1.0)[..., None], 0.0)
+    return o, lse

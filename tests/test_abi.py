@@ -28,8 +28,8 @@ def fa():
 
 
 def test_header_declares_the_api():
-    assert _declared_functions() == ["fa_abi_version", "fa_fwd", "fa_fwd_fp8", "fa_quant_rotate_fp8",
-                                     "fa_status_string"]
+    assert _declared_functions() == ["fa_abi_version", "fa_fwd", "fa_fwd_fp8", "fa_fwd_partial", "fa_merge",
+                                     "fa_quant_rotate_fp8", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -111,3 +111,38 @@ def test_product_path_has_no_cpu_fallback():
             src = open(os.path.join(pkg, fn)).read()
             assert "oracle" not in src.replace("oracle_", ""), fn
             assert "scaled_dot_product_attention" not in src and "softmax" not in src, fn
+
+
+def _partial(fa, q=P, k=P2, v=P3, o=P4, lse=P5, B=1, H=1, Nq=64, Nk=128, d=64, pos0=0, kb=0, ke=128, causal=1,
+             scale=0.125, dtype=1):
+    return fa.load_library().fa_fwd_partial(q, k, v, o, lse, B, H, Nq, Nk, d, pos0, kb, ke, causal, scale, dtype,
+                                            None)
+
+
+def test_partial_validation(fa):
+    assert _partial(fa, kb=-1) == fa.FA_ERR_SHAPE
+    assert _partial(fa, kb=50, ke=40) == fa.FA_ERR_SHAPE       # reversed range
+    assert _partial(fa, ke=129) == fa.FA_ERR_SHAPE             # past the keys
+    assert _partial(fa, pos0=-1) == fa.FA_ERR_SHAPE
+    assert _partial(fa, pos0=2 ** 30) == fa.FA_ERR_SHAPE       # positions beyond 32-bit arithmetic
+    assert _partial(fa, dtype=0) == fa.FA_ERR_UNSUPPORTED      # bf16 only
+    assert _partial(fa, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert _partial(fa, causal=3) == fa.FA_ERR_UNSUPPORTED
+    assert _partial(fa, scale=float("nan")) == fa.FA_ERR_SCALE
+    assert _partial(fa, o=None) == fa.FA_ERR_NULL
+    assert _partial(fa, o=ctypes.c_void_p(0x10000 + 32)) == fa.FA_ERR_ALIAS  # o_part overlaps q
+    assert _partial(fa, q=None, k=None, v=None, o=None, lse=None, Nq=0) == fa.FA_OK
+
+
+def _merge(fa, op=P, lp=P2, n=3, o=P3, lse=P4, B=1, H=1, N=64, d=64, dtype=1):
+    return fa.load_library().fa_merge(op, lp, n, o, lse, B, H, N, d, dtype, None)
+
+
+def test_merge_validation(fa):
+    assert _merge(fa, n=0) == fa.FA_ERR_SHAPE
+    assert _merge(fa, N=-1) == fa.FA_ERR_SHAPE
+    assert _merge(fa, d=32) == fa.FA_ERR_UNSUPPORTED
+    assert _merge(fa, dtype=5) == fa.FA_ERR_UNSUPPORTED
+    assert _merge(fa, op=None) == fa.FA_ERR_NULL
+    assert _merge(fa, o=ctypes.c_void_p(0x10000 + 64)) == fa.FA_ERR_ALIAS  # o inside o_parts
+    assert _merge(fa, op=None, lp=None, o=None, lse=None, N=0) == fa.FA_OK

@@ -16,15 +16,6 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.fixture(scope="module")
-def fa():
-    if not torch.cuda.is_available():
-        pytest.fail("GPU tests need a GPU")
-    import exact_tiled_attention_18_amd as fa
-    fa.load_library()
-    return fa
-
-
 def _run(fa, q, k, v, causal, scale):
     o, lse = fa.fa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale)
     torch.cuda.synchronize()

@@ -1,0 +1,111 @@
+"""GPU parity of the split-KV path: fa_fwd_partial and fa_merge against the oracle.
+
+fa_fwd_partial runs the bf16 forward kernel on one key range with queries at an
+offset position; its O is fp32 but the probabilities feeding P V are rounded to
+bf16 as in fa_fwd, so O carries the bf16 bound (2e-2) and LSE the 1e-3 one.
+Rows that see no key of the range must come back exactly O = 0, LSE = -inf.
+fa_merge is pure fp32 arithmetic: O within 1e-5 (fp32 output; bf16 output
+within its rounding), LSE within 1e-5."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import attention as A
+from tests import gpu_checks as G
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL_O, TOL_L = 2e-2, 1e-3
+
+# (Nq, Nk, q_pos0, k_begin, k_end, causal, d)
+CASES = [
+    (128, 128, 0, 0, 128, True, 128),      # the square problem over its full range
+    (16, 1000, 984, 0, 1000, True, 128),   # decode: the last 16 positions of 1000
+    (300, 700, 400, 256, 641, True, 128),  # offset queries, a range ending mid-tile
+    (300, 700, 400, 256, 641, False, 64),
+    (64, 64, 0, 10, 10, False, 128),       # empty range
+    (32, 600, 0, 500, 600, True, 64),      # every query before the range: nothing visible
+    (100, 333, 0, 17, 333, False, 64),     # ragged range
+    (257, 513, 100, 0, 290, True, 128),    # some rows see nothing, others part of the range
+    (1, 5000, 4999, 1234, 4999, True, 128),
+]
+
+
+def _inputs(nq, nk, d, seed):
+    q, _, _ = synthetic.draw_qkv(2, 3, nq, d, seed=seed, dtype="bf16")
+    _, k, v = synthetic.draw_qkv(2, 3, nk, d, seed=seed + 1, dtype="bf16")
+    return q, k, v
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "q{}k{}p{}r{}-{}{}d{}".format(c[0], c[1], c[2], c[3], c[4],
+                                                                                     "c" if c[5] else "", c[6]))
+def test_partial(fa, case):
+    nq, nk, pos0, kb, ke, causal, d = case
+    G.log(f"case partial {case}")
+    q, k, v = _inputs(nq, nk, d, seed=nq + nk + d)
+    scale = d ** -0.5
+    o, lse = fa.fa_fwd_partial(q.to(DEV), k.to(DEV), v.to(DEV), pos0, kb, ke, causal, scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = A.partial(q, k, v, causal, scale, pos0, kb, ke)
+    o, lse = o.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    empty = ~np.isfinite(l_ref)
+    assert np.array_equal(~np.isfinite(lse), empty)
+    assert np.all(lse[empty] == -np.inf) and not o[empty].any()
+    live = ~empty
+    eo = np.abs(o[live] - o_ref[live]).max() if live.any() else 0.0
+    el = np.abs(lse[live] - l_ref[live]).max() if live.any() else 0.0
+    G.log(f"  max|dO| {eo:.3e}  max|dLSE| {el:.3e}  empty rows {int(empty.sum())}")
+    assert eo <= TOL_O and el <= TOL_L
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_merge(fa, d, dtype):
+    G.log(f"case merge d={d} {dtype}")
+    rng = np.random.default_rng(d)
+    n, B, H, N = 5, 2, 3, 77
+    o_parts = rng.standard_normal((n, B, H, N, d)).astype(np.float32)
+    lse_parts = (3.0 * rng.standard_normal((n, B, H, N))).astype(np.float32)
+    lse_parts[rng.random((n, B, H, N)) < 0.3] = -np.inf   # ranges a row does not see
+    lse_parts[:, 0, 0, :5] = -np.inf                       # rows that see nothing at all
+    o, lse = fa.fa_merge(torch.from_numpy(o_parts).to(DEV), torch.from_numpy(lse_parts).to(DEV), dtype)
+    torch.cuda.synchronize()
+    o_ref, l_ref = A.merge(o_parts, lse_parts)
+    o, lse = o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    assert np.all(lse[0, 0, :5] == -np.inf) and not o[0, 0, :5].any()
+    live = np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(lse), live)
+    tol_o = 1e-5 if dtype == torch.float32 else 2.0 ** -8 * (1.0 + np.abs(o_ref[live]))
+    assert np.all(np.abs(o[live] - o_ref[live]) <= tol_o)
+    assert np.abs(lse[live] - l_ref[live]).max() <= 1e-5
+
+
+@pytest.mark.parametrize("n_splits", [1, 3, 8])
+def test_split_kv_decode(fa, n_splits):
+    """Decode-shaped split-KV forward: 16 new queries against 4096 cached keys."""
+    G.log(f"case split-KV decode n_splits={n_splits}")
+    nq, nk, d = 16, 4096, 128
+    q, k, v = _inputs(nq, nk, d, seed=99)
+    o, lse = fa.split_kv_attention(q.to(DEV), k.to(DEV), v.to(DEV), n_splits, causal=True, scale=d ** -0.5)
+    torch.cuda.synchronize()
+    o_ref, l_ref = A.partial(q, k, v, True, d ** -0.5, nk - nq, 0, nk)
+    eo = np.abs(o.float().cpu().numpy() - o_ref).max()
+    el = np.abs(lse.cpu().numpy() - l_ref).max()
+    G.log(f"  max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+    assert eo <= TOL_O and el <= TOL_L
+
+
+def test_split_kv_square_matches_full_forward(fa):
+    """The square causal problem split in four key ranges equals fa_fwd within bf16 rounding."""
+    q, k, v = _inputs(1024, 1024, 128, seed=5)
+    k, v = synthetic.draw_qkv(2, 3, 1024, 128, seed=6, dtype="bf16")[1:]
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o_s, l_s = fa.split_kv_attention(qd, kd, vd, 4, causal=True)
+    o_f, l_f = fa.fa_fwd(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = A.reference(q, k, v, True, 128 ** -0.5, rows=np.arange(0, 1024, 37))
+    for o, l in ((o_s, l_s), (o_f, l_f)):
+        o = o.float().cpu().numpy()[:, :, ::37]
+        l = l.cpu().numpy()[:, :, ::37]
+        assert np.abs(o - o_ref).max() <= TOL_O and np.abs(l - l_ref).max() <= TOL_L

@@ -189,3 +189,37 @@ def merge(o_parts, lse_parts):
     lse = np.where(alive, np.where(alive, m, 0.0) + np.log(np.where(alive, z, 1.0)), -np.inf)
     o = np.where(alive[..., None], (w[..., None] * o_parts).sum(axis=0) / np.where(alive, z, 1.0)[..., None], 0.0)
     return o, lse
+
+
+def backward(q, k, v, do, causal: bool, scale: float):
+    """Gradients of attention for [B, H, N, d] inputs and output gradient dO.
+
+    With S = scale * Q K^T (masked), P = softmax(S) row by row and O = P V, the
+    chain rule gives, per head:
+      dV = P^T dO
+      dP = dO V^T
+      D_i = sum_j P_ij dP_ij  (= sum_c dO_ic O_ic)
+      dS = P * (dP - D)        (the softmax Jacobian applied row by row)
+      dQ = scale * dS K,   dK = scale * dS^T Q.
+    This is the quantity the pages' training use needs from the saved LSE
+    (FlashAttention-2 wiki page, "Leistung und Effizienz": end-to-end training);
+    here it is written from the plain definition, materialising P.
+    Returns (dQ, dK, dV) as float64 arrays.
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    B, H, N, d = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    rows = np.arange(N)
+    for b in range(B):
+        for h in range(H):
+            s = _scores(q[b, h], k[b, h], scale, causal, rows)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            p = e / e.sum(axis=1, keepdims=True)
+            dv[b, h] = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, h].T
+            dd = (p * dp).sum(axis=1, keepdims=True)
+            ds = p * (dp - dd)
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ q[b, h])
+    return dq, dk, dv

@@ -204,6 +204,40 @@ def cpu_baseline(w, budget_s: float):
                       f"full N x N fp64 oracle, {dt:.1f} s"}
 
 
+def bench_backward(fa, w, dev, args):
+    """One step = one fa_bwd call (delta, dQ, dK/dV kernels).  FLOPs counted as
+    2.5x the forward's (five matrix products of the same size; the kernels
+    recompute S and dP in both passes, which is not counted)."""
+    if w.dtype != "bf16":
+        raise SystemExit("the backward pass is provided for bf16 workloads")
+    q, k, v, _ = synthetic.workload_inputs(w)
+    do = synthetic.draw_qkv(w.B, w.H, w.N, w.d, seed=w.seed + 100, dtype="bf16")[0]
+    q, k, v, do = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fa.fa_fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sec = time_loop(step, args.steps)
+    flops = 2.5 * w.flops()
+    tflops = flops / sec / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    eprint(f"{w.name} backward: {sec * 1e6:.1f} us = {tflops:.1f} TFLOP/s = {tflops / peak:.1%} of {peak}")
+    rec = {"metric": "attention bwd TFLOP/s at 1 MI355X (2.5x forward FLOPs)", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": w.name, "pass": "backward", "flops_per_step": flops},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(tflops / peak, 4), "traffic": None},
+           "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +247,8 @@ def main():
                     choices=[w.name for w in synthetic.WORKLOADS])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (fa_bwd) of a bf16 workload instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -238,6 +274,8 @@ def main():
     w = synthetic.workload(args.workload)
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib, dev)
+    if args.backward:
+        return bench_backward(fa, w, dev, args)
     step, parts = make_step(fa, w, dev)
     for _ in range(args.warmup):
         step()

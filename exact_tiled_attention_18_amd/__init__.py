@@ -57,6 +57,8 @@ def load_library():
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, f32, vp]
     lib.fa_fwd_partial.restype = i32
     lib.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd.argtypes = [vp] * 10 + [i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_merge.restype = i32
     lib.fa_merge.argtypes = [vp, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp]
     _lib = lib
@@ -234,3 +236,26 @@ def split_kv_attention(q, k, v, n_splits: int, causal: bool = False, scale: floa
         fa_fwd_partial(q, k, v, q_pos0, bounds[i], bounds[i + 1], causal, scale, o_part=o_parts[i],
                        lse_part=lse_parts[i], stream=stream)
     return fa_merge(o_parts, lse_parts, q.dtype, stream=stream)
+
+
+def fa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
+           delta=None, stream=None):
+    """dQ, dK, dV (bfloat16 [B, H, N, d]) for bfloat16 q, k, v, the forward's o and lse,
+    and the output gradient dout.  delta (float32 [B, H, N]) is a workspace."""
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_dense(q, k, v, o, dout, lse, dq, dk, dv, delta)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, (B, H, N, d), torch.bfloat16, name)
+    _expect(lse, (B, H, N), torch.float32, "lse")
+    _expect(delta, (B, H, N), torch.float32, "delta")
+    lib = load_library()
+    _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      _ptr(delta), B, H, N, d, int(causal), float(scale), FA_BF16, _stream(stream)))
+    return dq, dk, dv

@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "attn_f32.hip", "attn_bf16.hip", "quant_fp8.hip", "attn_fp8.hip", "merge.hip"]
+SOURCES = ["api.hip", "attn_f32.hip", "attn_bf16.hip", "quant_fp8.hip", "attn_fp8.hip", "merge.hip", "attn_bwd.hip"]
 EXTRA = {}  # per-source extra flags
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

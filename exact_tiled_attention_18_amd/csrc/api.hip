@@ -172,4 +172,36 @@ int fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void
   return hip_status(fa::launch_merge(a));
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+           float scale, int dtype, void* stream) {
+  int64_t n = 0;
+  if (int st = shape_status(B, H, N, d, &n)) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (n == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  const void* in16[] = {q, k, v, o, dout};
+  for (const void* p : in16)
+    if (!aligned(p, 16)) return FA_ERR_UNSUPPORTED;
+  if (!aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+    return FA_ERR_UNSUPPORTED;
+  const int64_t tb = 2 * n, rb = 4 * B * H * N;
+  void* outs[] = {dq, dk, dv};
+  for (void* out : outs) {
+    for (const void* in : in16)
+      if (overlaps(out, tb, in, tb)) return FA_ERR_ALIAS;
+    if (overlaps(out, tb, lse, rb) || overlaps(out, tb, delta, rb)) return FA_ERR_ALIAS;
+  }
+  if (overlaps(dq, tb, dk, tb) || overlaps(dq, tb, dv, tb) || overlaps(dk, tb, dv, tb)) return FA_ERR_ALIAS;
+  for (const void* in : in16)
+    if (overlaps(delta, rb, in, tb)) return FA_ERR_ALIAS;
+  if (overlaps(delta, rb, lse, rb)) return FA_ERR_ALIAS;
+  const fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale,
+                      static_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_attn_bwd(a));
+}
+
 }  // extern "C"

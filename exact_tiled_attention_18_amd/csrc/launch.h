@@ -45,6 +45,25 @@ struct MergeArgs {
 };
 hipError_t launch_merge(const MergeArgs& a);
 
+// Backward pass (bf16): dQ, dK, dV from Q, K, V, O, dO and the saved LSE.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [B, H, N] workspace: rowsum(dO * O)
+  int64_t B, H, N, d;
+  int causal;
+  float scale;
+  hipStream_t stream;
+};
+hipError_t launch_attn_bwd(const BwdArgs& a);
+
 struct QuantArgs {
   const void* x;
   uint8_t* x8;

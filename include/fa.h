@@ -174,6 +174,31 @@ int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, f
 int fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* stream);
 
+/*
+ * fa_bwd -- attention backward: the gradients dQ, dK, dV of the forward
+ * output for an output gradient dO, recomputing the probabilities tile by
+ * tile from the LSE the forward saved (training is the pages' motivating use:
+ * FlashAttention-2 wiki page, "Leistung und Effizienz").  With S = scale Q K^T
+ * (masked), P = softmax(S):  dV = P^T dO;  D = rowsum(dO * O);
+ * dS = P * (dO V^T - D);  dQ = scale dS K;  dK = scale dS^T Q.
+ *   q, k, v, o, dout : bfloat16 [B, H, N, d] (o: the forward's output).
+ *   lse              : float32 [B, H, N], the forward's logsumexp.
+ *   dq, dk, dv       : bfloat16 [B, H, N, d], fully overwritten.
+ *   delta            : float32 [B, H, N] workspace (caller-owned), overwritten
+ *                      with D.
+ *   d: 64 or 128.  dtype: FA_BF16.  causal: 0 or 1.  scale: finite, the one
+ *   the forward used.
+ * Arithmetic: products on bf16 MFMA with fp32 accumulation; P and dS are
+ * rounded to bf16 for the products that use them; no atomics (bitwise
+ * reproducible).
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, dtype, causal,
+ * alignment), FA_ERR_SCALE, FA_ERR_ALIAS (any output or the workspace
+ * overlapping an input or each other), FA_ERR_HIP.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
+           int64_t N, int64_t d, int causal, float scale, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,8 +28,8 @@ def fa():
 
 
 def test_header_declares_the_api():
-    assert _declared_functions() == ["fa_abi_version", "fa_fwd", "fa_fwd_fp8", "fa_fwd_partial", "fa_merge",
-                                     "fa_quant_rotate_fp8", "fa_status_string"]
+    assert _declared_functions() == ["fa_abi_version", "fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_partial",
+                                     "fa_merge", "fa_quant_rotate_fp8", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -146,3 +146,22 @@ def test_merge_validation(fa):
     assert _merge(fa, op=None) == fa.FA_ERR_NULL
     assert _merge(fa, o=ctypes.c_void_p(0x10000 + 64)) == fa.FA_ERR_ALIAS  # o inside o_parts
     assert _merge(fa, op=None, lp=None, o=None, lse=None, N=0) == fa.FA_OK
+
+
+def _bwd(fa, q=P, k=P2, v=P3, o=P4, do=P5, lse=ctypes.c_void_p(0x7A000000), dq=ctypes.c_void_p(0x7C000000),
+         dk=ctypes.c_void_p(0x7E000000), dv=ctypes.c_void_p(0x80000000), delta=ctypes.c_void_p(0x82000000),
+         B=1, H=1, N=128, d=64, causal=1, scale=0.125, dtype=1):
+    return fa.load_library().fa_bwd(q, k, v, o, do, lse, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, None)
+
+
+def test_bwd_validation(fa):
+    assert _bwd(fa, N=-1) == fa.FA_ERR_SHAPE
+    assert _bwd(fa, d=32) == fa.FA_ERR_UNSUPPORTED
+    assert _bwd(fa, dtype=0) == fa.FA_ERR_UNSUPPORTED
+    assert _bwd(fa, causal=2) == fa.FA_ERR_UNSUPPORTED
+    assert _bwd(fa, scale=float("inf")) == fa.FA_ERR_SCALE
+    assert _bwd(fa, delta=None) == fa.FA_ERR_NULL
+    assert _bwd(fa, dq=ctypes.c_void_p(0x10000 + 64)) == fa.FA_ERR_ALIAS  # dq overlaps q
+    assert _bwd(fa, dk=ctypes.c_void_p(0x7C000000 + 32)) == fa.FA_ERR_ALIAS  # dk overlaps dq
+    assert _bwd(fa, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, delta=None,
+                N=0) == fa.FA_OK

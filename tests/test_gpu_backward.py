@@ -1,0 +1,89 @@
+"""GPU parity of the backward pass: fa_bwd against the oracle's fp64 gradients.
+
+The kernel recomputes P from the forward's fp32 LSE, takes D from the bf16 O
+of the forward, rounds P and dS to bf16 for the products that use them and
+rounds the gradients to bf16 once.  The bound compares each gradient tensor
+of a head normwise, max |g - g_ref| / max(1, max |g_ref|) <= 2e-2: the same
+budget as the bf16 forward output (whose magnitude is O(1)), here relative to
+the tensor's largest entry where that exceeds 1, because gradient magnitudes
+scale with the scale, N and the inputs (with one key, dQ and dK vanish
+exactly and only rounding remains)."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import attention as A
+from tests import gpu_checks as G
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = 2e-2
+
+
+def _grads(fa, q, k, v, do, causal, scale):
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa.fa_fwd(qd, kd, vd, causal=causal, scale=scale)
+    dq, dk, dv = fa.fa_bwd(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def _errors(got, ref):
+    out = []
+    for g, r in zip(got, ref):
+        g = g.float().cpu().numpy().astype(np.float64)
+        den = max(np.abs(r).max(), 1.0)
+        out.append(float(np.abs(g - r).max() / den))
+    return out
+
+
+SMALL = [(1, 2, n, d) for n in (1, 7, 64, 100, 129, 300, 513) for d in (64, 128)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}N{}d{}".format(*s))
+def test_backward_small(fa, shape, causal):
+    B, H, N, d = shape
+    G.log(f"case backward {shape} causal={causal}")
+    q, k, v = synthetic.draw_qkv(B, H, N, d, seed=N * 7 + d, dtype="bf16")
+    do = synthetic.draw_qkv(B, H, N, d, seed=N * 7 + d + 1, dtype="bf16")[0]
+    got = _grads(fa, q, k, v, do, causal, d ** -0.5)
+    ref = A.backward(q, k, v, do, causal, d ** -0.5)
+    e = _errors(got, ref)
+    G.log(f"  normwise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
+    assert max(e) <= TOL
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.15, 0.5])
+def test_backward_scales(fa, scale):
+    B, H, N, d = 1, 2, 200, 128
+    G.log(f"case backward scale={scale}")
+    q, k, v = synthetic.draw_qkv(B, H, N, d, seed=31, dtype="bf16")
+    do = synthetic.draw_qkv(B, H, N, d, seed=32, dtype="bf16")[0]
+    got = _grads(fa, q, k, v, do, True, scale)
+    ref = A.backward(q, k, v, do, True, scale)
+    if scale == 0.0:  # S does not depend on Q or K: their gradients vanish
+        assert not got[0].float().abs().max().item() and not got[1].float().abs().max().item()
+        e = _errors(got[2:], ref[2:])
+    else:
+        e = _errors(got, ref)
+    G.log(f"  normwise errors {['%.2e' % x for x in e]}")
+    assert max(e) <= TOL
+
+
+def test_backward_full_size_heads(fa):
+    """The bench's bf16 workload (B4 H16 N2048 d128 causal) in its launch configuration, two heads checked."""
+    w = synthetic.workload("bf16_causal_b4h16n2048d128")
+    G.log(f"case backward {w.name}")
+    q, k, v, _ = synthetic.workload_inputs(w)
+    do = synthetic.draw_qkv(w.B, w.H, w.N, w.d, seed=w.seed + 100, dtype="bf16")[0]
+    got = _grads(fa, q, k, v, do, w.causal, w.scale)
+    for b, h in ((0, 0), (3, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = A.backward(q[sl], k[sl], v[sl], do[sl], w.causal, w.scale)
+        e = _errors([x[sl] for x in got], ref)
+        G.log(f"  head ({b},{h}) normwise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
+        assert max(e) <= TOL
+    again = _grads(fa, q, k, v, do, w.causal, w.scale)
+    assert all(torch.equal(x, y) for x, y in zip(got, again))  # no atomics: bitwise reproducible

@@ -133,6 +133,19 @@ def test_fp8_small(fa, N, causal, outliers):
     assert rel <= G.FP8_O_TOL and el <= G.FP8_LSE_TOL
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.15, 0.5])
+def test_fp8_scales(fa, scale):
+    """Negative scale (every Q code's sign bit flipped), zero scale (Q zeroed), large scale."""
+    G.log(f"case fp8 scale={scale}")
+    d, N = 128, 300
+    q, k, v = synthetic.draw_qkv(1, 2, N, d, seed=41, dtype="bf16")
+    signs = synthetic.draw_signs(d, 42)
+    o, lse, (q8, k8, v8t, qs, ks, vs) = _fp8_case(fa, q, k, v, signs, True, scale)
+    rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, True, scale, heads=[(0, 0), (0, 1)])
+    G.log(f"  vs dequantised oracle: scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
+    assert rel <= G.FP8_O_TOL and el <= G.FP8_LSE_TOL
+
+
 def test_fp8_workload_full_size(fa):
     w = synthetic.WORKLOADS[4]
     G.log(f"case workload {w.name}")

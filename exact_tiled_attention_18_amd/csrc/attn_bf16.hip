@@ -342,6 +342,29 @@ struct Attn {
     }
     __syncthreads();
   }
+
+  // ---- steps of a wavefront whose rows see no key of tile t or later (the causal
+  // diagonal of its workgroup): O += P_{t-1} V_{t-1} once, then only the workgroup's
+  // shared tile copies and the barrier, so that every wavefront passes the same barriers
+  template <int B>
+  __device__ __forceinline__ void step_pv(int t, int sk_w, int sv_pv, int sv_w) {
+    const bf16x8 (&pold)[kQB][2] = pbuf[B ^ 1];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      if (ch + 1 < NCH) vop[(ch + 1) & 1] = read_v(sv_pv, ch + 1);
+      const int db = ch % DB, mm = ch / DB;
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) oacc[db][qb] = mfma(vop[ch & 1], pold[qb][mm], oacc[db][qb]);
+    }
+    step_idle(t, sk_w, sv_w);
+  }
+  __device__ __forceinline__ void step_idle(int t, int sk_w, int sv_w) {
+    store_tile(kslot + sk_w * Ly::KSLOT, kst_off, Ly::KS, stg_k);
+    store_tile(vslot + sv_w * Ly::VSLOT, vst_off, Ly::VS, stg_v);
+    load_tile(krs, t + 4, stg_k);
+    load_tile(vrs, t + 2, stg_v);
+    __syncthreads();
+  }
 };
 
 // Rows of one launch: queries 0 .. nq-1 of each head against keys k0 .. k0+kn-1 of
@@ -493,18 +516,37 @@ __global__ __launch_bounds__(QB == 1 ? 512 : 256) void attn_fwd_bf16_kernel(
     s.template step<false, 0>(t + 1, sk_next, sk_w, sv_pv, sv_next, sv_w);
     advance();
   }
-  for (; t < nT; t += 2) {
+  // the wavefront's own last tile: the last one holding a key visible to one of its
+  // rows (wavefront-uniform; tiles up to nFull - 1 are visible to every row)
+  int last_w = CAUSAL ? min(gm.qpos + s.qw0 + kW - 1, gm.kn - 1) : gm.kn - 1;
+  last_w = __builtin_amdgcn_readfirstlane(last_w >= 0 ? last_w / kBc : -1);
+  const int t_end = min(nT, last_w + 1);
+  int tn = t;  // next tile
+  for (; t < t_end; t += 2) {
     s.template step<true, 1>(t, sk_next, sk_w, sv_pv, sv_next, sv_w);
     advance();
-    if (t + 1 < nT) {
+    tn = t + 1;
+    if (t + 1 < t_end) {
       s.template step<true, 0>(t + 1, sk_next, sk_w, sv_pv, sv_next, sv_w);
       advance();
+      tn = t + 2;
     }
   }
-
-  // last product: O += P_{nT-1} V_{nT-1} (operands of its first chunk read by the last step)
-  if ((nT - 1) & 1) s.template last_pv<1>((nT - 1) % kSlots);
-  else s.template last_pv<0>((nT - 1) % kSlots);
+  if (tn < nT) {
+    // tiles tn .. nT-1 hold no key this wavefront's rows see: the product of its last
+    // tile (operands of its first chunk read by the last step), then copies only
+    if (tn & 1) s.template step_pv<1>(tn, sk_w, sv_pv, sv_w);
+    else s.template step_pv<0>(tn, sk_w, sv_pv, sv_w);
+    advance();
+    for (int u = tn + 1; u < nT; ++u) {
+      s.step_idle(u, sk_w, sv_w);
+      advance();
+    }
+  } else {
+    // last product: O += P_{nT-1} V_{nT-1} (operands of its first chunk read by the last step)
+    if ((nT - 1) & 1) s.template last_pv<1>((nT - 1) % kSlots);
+    else s.template last_pv<0>((nT - 1) % kSlots);
+  }
 
   // ---- epilogue: the single division by the row sum, LSE, stores
 #pragma unroll

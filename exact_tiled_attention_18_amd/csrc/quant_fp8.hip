@@ -174,6 +174,79 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
   }
 }
 
+// Transposed output without rotation (the V operand): thread (cg, j) loads the R
+// consecutive rows R*j .. R*j+R-1 of the tile in columns 8cg .. 8cg+7 (R = 8 at
+// d = 128, 4 at d = 64), so for each of its columns it holds R codes that go to
+// LDS as one R-byte word, in 16-byte chunks of a column row whose order is
+// XOR-swizzled by the column group (the column groups of a wavefront would
+// otherwise write the same banks).
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_transpose_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ x8, float* __restrict__ x_scale, int N, int nTiles) {
+  constexpr int CG = D / 8;                      // column groups
+  constexpr int R = kTileRows * CG / kThreads;   // rows per thread
+  static_assert(R == 4 || R == 8, "4 or 8 rows per thread");
+  constexpr int LD = kTileRows + 16;             // LDS bytes per column row (16-byte aligned)
+  __shared__ float red[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) uint8_t tr[D * LD];
+
+  const int tile = blockIdx.x % nTiles;
+  const int bh = blockIdx.x / nTiles;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG, j = tid / CG;
+  const int r0 = tile * kTileRows;
+  const size_t base = (size_t)bh * N * D;
+
+  float z[R][8];  // [row][column]
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int row = r0 + R * j + i;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (row < N) w = *reinterpret_cast<const uint4*>(x + base + (size_t)row * D + cg * 8);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[i][e] = __uint_as_float((e & 1) ? (ww[e >> 1] & 0xFFFF0000u) : (ww[e >> 1] << 16));
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(z[i][e]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float mult = amax > 0.f ? 448.0f / amax : 1.0f;
+  if (tid == 0) x_scale[(size_t)bh * nTiles + tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+
+  const int pos = R * j;  // byte position of this thread's rows in a column row
+  const int off = (((pos >> 4) ^ (cg & 7)) << 4) + (pos & 15);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint8_t* t = &tr[(cg * 8 + e) * LD + off];
+    // rows past N hold zeros, whose code is 0
+    const uint32_t lo = e4m3x4(z[0][e] * mult, z[1][e] * mult, z[2][e] * mult, z[3][e] * mult);
+    if constexpr (R == 8) {
+      const uint32_t hi = e4m3x4(z[4][e] * mult, z[5][e] * mult, z[6][e] * mult, z[7][e] * mult);
+      *reinterpret_cast<uint2*>(t) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<uint32_t*>(t) = lo;
+    }
+  }
+  __syncthreads();
+  // x8 is [B, H, D, N64]: row `col` of this head holds the codes of all N rows,
+  // then code 0 up to N64
+  const int ldv = (N + 63) / 64 * 64;
+  const int chunks = min(kTileRows, ldv - r0) / 16;
+  uint8_t* dst = x8 + (size_t)bh * D * ldv + r0;
+  for (int i = tid; i < D * chunks; i += kThreads) {
+    const int col = i / chunks, ch = i % chunks;
+    *reinterpret_cast<uint4*>(dst + (size_t)col * ldv + ch * 16) =
+        *reinterpret_cast<const uint4*>(&tr[col * LD + ((ch ^ ((col >> 3) & 7)) << 4)]);
+  }
+}
+
 template <int D>
 hipError_t launch_d(const QuantArgs& a) {
   const int BH = (int)(a.B * a.H), N = (int)a.N;
@@ -187,7 +260,7 @@ hipError_t launch_d(const QuantArgs& a) {
       hipLaunchKernelGGL((quant_rotate_kernel<D, true, false>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
   } else {
     if (a.transpose_out)
-      hipLaunchKernelGGL((quant_rotate_kernel<D, false, true>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
+      hipLaunchKernelGGL((quant_transpose_kernel<D>), grid, block, 0, a.stream, x, a.x8, a.x_scale, N, nTiles);
     else
       hipLaunchKernelGGL((quant_rotate_kernel<D, false, false>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
   }

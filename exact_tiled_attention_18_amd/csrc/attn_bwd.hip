@@ -25,7 +25,11 @@
 //              out as B operands of dV^T += dO^T P and dK^T += Q^T dS.
 // Tiles are double-buffered: the next tile is loaded into registers while the
 // current one is used, then written to the other buffer before the step's
-// single barrier.
+// single barrier.  At d = 128 the dK/dV kernel is software-pipelined instead
+// (four tile buffers; each step interleaves the score MFMAs of the next tile,
+// the gradient MFMAs of the previous one and the vector work of the current
+// one); at d = 64 the plain kernel keeps two wavefronts per SIMD, which hides
+// more than the pipeline does with one.
 //
 // A negative scale flips every sign bit of Q, a zero scale zeroes Q (the
 // kernels then use the positive multiplier |scale| * log2(e)): dQ = scale *
@@ -376,6 +380,265 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   }
 }
 
+// ---------------------------------------------------------------- dK, dV (d = 128)
+// Software pipeline over query tiles: step t issues the MFMAs of S_{t+1} = Q'_{t+1} K^T
+// and dP_{t+1} = dO_{t+1} V^T, the MFMAs of dV += dO_{t-1}^T P_{t-1} and
+// dK += Q'_{t-1}^T dS_{t-1}, and the vector work that turns S_t, dP_t into P_t, dS_t;
+// none depends on another, so they are interleaved chunk by chunk.  Four LDS
+// buffers hold tiles t-1 .. t+2 (tile t waits there for its dV/dK products in the
+// next step); tile t+2 is written from registers loaded one step earlier.
+template <int D, bool CAUSAL>
+struct DkDv {
+  using T = Tile<D>;
+  static constexpr int DK = D / 16, DB = D / 32, NB = 4;
+  static constexpr int kPer = T::PIECES / 256;  // 16-byte pieces per thread and operand tile (1 or 2)
+  static constexpr int EPC = 16 / DK;           // score elements per chunk (2 or 4)
+  static_assert(DK == 2 * DB, "one dV/dK operand pair per chunk");
+
+  bf16x8 kf[DK], vf[DK];
+  f32x16 dva[DB], dka[DB];
+  f32x16 s[2], dp[2];        // S and dP of tiles t (parity B) and t+1
+  uint32_t pw[2][8], sw[2][8];  // P and dS (bf16 pairs) of tiles t (parity B) and t-1
+  bf16x8 opq[2], opd[2], opv[2], opk[2];  // operands of the next chunk
+  uint4 sq[kPer], sd[kPer];
+  float sstat;
+  float ls[16], dl[16];
+
+  char* smem;
+  float* stat;  // [NB][2][kT]
+  __amdgpu_buffer_rsrc_t qrs, drs;
+  const float* lse_h;
+  const float* delta_h;
+  int N, tid, g, li, kj, qrow, tr_off;
+  int ld_off[kPer], st_off[kPer];
+  float c;
+  uint32_t qxor, qand;
+
+  __device__ __forceinline__ char* qbuf(int b) const { return smem + b * T::BYTES; }
+  __device__ __forceinline__ char* dbuf(int b) const { return smem + (NB + b) * T::BYTES; }
+
+  __device__ __forceinline__ void load(int t) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ld_off[i] + t * kT * D * 2, 0, 0));
+      sq[i] = make_uint4((a.x ^ qxor) & qand, (a.y ^ qxor) & qand, (a.z ^ qxor) & qand, (a.w ^ qxor) & qand);
+      sd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, ld_off[i] + t * kT * D * 2, 0, 0));
+    }
+    if (tid < 2 * kT) {
+      const int row = t * kT + (tid & (kT - 1));
+      sstat = row < N ? (tid < kT ? lse_h[row] * kLog2e : delta_h[row]) : 0.f;
+    }
+  }
+  __device__ __forceinline__ void store(int b) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      *reinterpret_cast<uint4*>(qbuf(b) + st_off[i]) = sq[i];
+      *reinterpret_cast<uint4*>(dbuf(b) + st_off[i]) = sd[i];
+    }
+    if (tid < 2 * kT) stat[(b * 2 + tid / kT) * kT + (tid & (kT - 1))] = sstat;
+  }
+  // LSE and D of this lane's 16 queries (two runs of 8) of the tile in buffer b
+  __device__ __forceinline__ void read_stats(int b) {
+    const float4* sl = reinterpret_cast<const float4*>(stat + (b * 2) * kT);
+    const float4* sdl = reinterpret_cast<const float4*>(stat + (b * 2 + 1) * kT);
+    const float4 a0 = sl[2 * g], a1 = sl[2 * g + 1], a2 = sl[4 + 2 * g], a3 = sl[5 + 2 * g];
+    const float4 b0 = sdl[2 * g], b1 = sdl[2 * g + 1], b2 = sdl[4 + 2 * g], b3 = sdl[5 + 2 * g];
+    const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w, a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+    const float bv[16] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w, b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ls[r] = av[r];
+      dl[r] = bv[r];
+    }
+  }
+  // P and dS of score elements [e0, e0 + EPC) of tile t (parity B)
+  template <int B>
+  __device__ __forceinline__ void grad_slice(int t, int e0) {
+#pragma unroll
+    for (int e = e0; e < e0 + EPC; e += 2) {
+      float p2[2], d2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = e + h;
+        const int qr = t * kT + row_of_reg(r, g);
+        const bool vis = qr < N && kj < N && (!CAUSAL || kj <= qr);
+        p2[h] = vis ? exp2_fast(fmaf(s[B][r], c, -ls[r])) : 0.f;
+        d2[h] = p2[h] * (dp[B][r] - dl[r]);
+      }
+      pw[B][e >> 1] = pack_bf16x2(p2[0], p2[1]);
+      sw[B][e >> 1] = pack_bf16x2(d2[0], d2[1]);
+    }
+  }
+  __device__ __forceinline__ bf16x8 word8(const uint32_t (&w)[8], int mm) const {
+    return __builtin_bit_cast(bf16x8, make_uint4(w[4 * mm], w[4 * mm + 1], w[4 * mm + 2], w[4 * mm + 3]));
+  }
+  // operands of chunk ch: S/dP operands of the tile in buffer bn, dV/dK operands of buffer bo
+  __device__ __forceinline__ void read_sdp(int slot, int ch, int bn) {
+    opq[slot] = read_row<D>(qbuf(bn), qrow, ch, g);
+    opd[slot] = read_row<D>(dbuf(bn), qrow, ch, g);
+  }
+  __device__ __forceinline__ void read_grad(int slot, int ch, int bo) {
+    opv[slot] = read_tr<D>(dbuf(bo), tr_off, ch % DB, ch / DB);
+    opk[slot] = read_tr<D>(qbuf(bo), tr_off, ch % DB, ch / DB);
+  }
+
+  // one step for tile t in buffer cur (parity B = (t - t0) & 1); the dV/dK operands
+  // of its chunk 0 were read by the previous step (tile t+1's were written before
+  // the last barrier only, so its S/dP operands are read here)
+  template <int B>
+  __device__ __forceinline__ void step(int t, int cur, bool more) {
+    const int bn = (cur + 1) % NB, bo = (cur + NB - 1) % NB, bw = (cur + 2) % NB;
+    read_sdp(0, 0, bn);
+    read_stats(cur);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[B ^ 1][r] = dp[B ^ 1][r] = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {
+      if (ch + 1 < DK) {
+        read_sdp((ch + 1) & 1, ch + 1, bn);
+        read_grad((ch + 1) & 1, ch + 1, bo);
+      } else {
+        read_grad(0, 0, cur);  // the next step's chunk 0: dV/dK operands of tile t
+      }
+      const int sl = ch & 1, db = ch % DB, mm = ch / DB;
+      dva[db] = mfma(opv[sl], word8(pw[B ^ 1], mm), dva[db]);
+      s[B ^ 1] = mfma(opq[sl], kf[ch], s[B ^ 1]);
+      dka[db] = mfma(opk[sl], word8(sw[B ^ 1], mm), dka[db]);
+      dp[B ^ 1] = mfma(opd[sl], vf[ch], dp[B ^ 1]);
+      grad_slice<B>(t, ch * EPC);
+      if (ch == 1) store(bw);
+      if (ch == 2 && more) load(t + 3);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);  // DS writes
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // VMEM reads
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  }
+  // dV/dK products of the last tile (parity B, buffer b); operands of chunk 0 read
+  template <int B>
+  __device__ __forceinline__ void last(int b) {
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {
+      const int db = ch % DB, mm = ch / DB;
+      const bf16x8 av = ch == 0 ? opv[0] : read_tr<D>(dbuf(b), tr_off, db, mm);
+      const bf16x8 ak = ch == 0 ? opk[0] : read_tr<D>(qbuf(b), tr_off, db, mm);
+      dva[db] = mfma(av, word8(pw[B], mm), dva[db]);
+      dka[db] = mfma(ak, word8(sw[B], mm), dka[db]);
+    }
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int BH, int N, float c, float dk_mul, uint32_t qxor,
+    uint32_t qand) {
+  using W = DkDv<D, CAUSAL>;
+  using T = Tile<D>;
+  constexpr int DK = W::DK, DB = W::DB, NB = W::NB, kPer = W::kPer, kBk = 128;
+  __shared__ __attribute__((aligned(16))) char smem[2 * NB * T::BYTES];  // Q' buffers, then dO buffers
+  __shared__ __attribute__((aligned(16))) float stat[NB * 2 * kT];       // [buffer][LSE*log2e, D][row]
+
+  W w;
+  const int L = blockIdx.x;
+  const int kblk = L / BH;  // smallest key blocks (most causal work) first
+  const int bh = L % BH;
+  const size_t base = (size_t)bh * N * D;
+  w.tid = threadIdx.x;
+  const int lane = w.tid & 63;
+  w.g = lane >> 5;
+  w.li = lane & 31;
+  const int k0 = kblk * kBk;
+  w.kj = k0 + (w.tid >> 6) * 32 + w.li;  // this lane's key
+  w.N = N;
+  w.c = c;
+  w.qxor = qxor;
+  w.qand = qand;
+  w.smem = smem;
+  w.stat = stat;
+  w.lse_h = lse + (size_t)bh * N;
+  w.delta_h = delta + (size_t)bh * N;
+  constexpr int kRsrcWord3 = 0x00020000;
+  w.qrs = __builtin_amdgcn_make_buffer_rsrc((void*)(q + base), (short)0, N * D * 2, kRsrcWord3);
+  w.drs = __builtin_amdgcn_make_buffer_rsrc((void*)(dout + base), (short)0, N * D * 2, kRsrcWord3);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int piece = w.tid + 256 * i;
+    const int prow = piece / (D / 8), pcol = (piece % (D / 8)) * 16;
+    w.ld_off[i] = prow * D * 2 + pcol;
+    w.st_off[i] = prow * T::S + pcol;
+  }
+  w.qrow = permuted_row(w.li);
+  w.tr_off = tr_offset<D>(lane);
+
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) {
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (w.kj < N) {
+      a = *reinterpret_cast<const uint4*>(k + base + (size_t)w.kj * D + ks * 16 + w.g * 8);
+      b = *reinterpret_cast<const uint4*>(v + base + (size_t)w.kj * D + ks * 16 + w.g * 8);
+    }
+    w.kf[ks] = __builtin_bit_cast(bf16x8, a);
+    w.vf[ks] = __builtin_bit_cast(bf16x8, b);
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.dva[db][r] = w.dka[db][r] = 0.f;
+
+  // query tiles that see any key of the block
+  const int t0 = CAUSAL ? k0 / kT : 0;
+  const int nQT = (N + kT - 1) / kT;
+  if (t0 < nQT) {
+    // prologue: tiles t0 and t0+1 into buffers 0 and 1, buffer 3 (tile t0-1 of the
+    // first step's dV/dK products) zeroed along with P_{t0-1} and dS_{t0-1}; S_t0, dP_t0
+    w.load(t0);
+    w.store(0);
+    w.load(t0 + 1);
+    w.store(1);
+    for (int i = w.tid; i < T::BYTES / 16; i += 256) {
+      *reinterpret_cast<uint4*>(w.qbuf(3) + 16 * i) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(w.dbuf(3) + 16 * i) = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w.pw[1][i] = w.sw[1][i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.s[0][r] = w.dp[0][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      w.s[0] = mfma(read_row<D>(w.qbuf(0), w.qrow, ks, w.g), w.kf[ks], w.s[0]);
+      w.dp[0] = mfma(read_row<D>(w.dbuf(0), w.qrow, ks, w.g), w.vf[ks], w.dp[0]);
+    }
+    w.load(t0 + 2);
+    w.read_grad(0, 0, 3);
+    int t = t0;
+    for (; t + 1 < nQT; t += 2) {
+      w.template step<0>(t, (t - t0) % NB, t + 3 < nQT);
+      w.template step<1>(t + 1, (t + 1 - t0) % NB, t + 4 < nQT);
+    }
+    if (t < nQT) {
+      w.template step<0>(t, (t - t0) % NB, t + 3 < nQT);
+      w.template last<0>((t - t0) % NB);
+    } else {
+      w.template last<1>((t - 1 - t0) % NB);
+    }
+  }
+  if (w.kj < N) {
+    store_rows<D>(dv + base + (size_t)w.kj * D, w.dva, 1.f, w.g);
+    store_rows<D>(dk + base + (size_t)w.kj * D, w.dka, dk_mul, w.g);
+  }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_d(const BwdArgs& a) {
   const int BH = (int)(a.B * a.H), N = (int)a.N;
@@ -394,9 +657,16 @@ hipError_t launch_d(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v, dout,
                      a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
   const int nKB = (N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(256), 0, a.stream, q, k, v,
-                     dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N, c,
-                     fabsf(a.scale), qxor, qand);
+  // d = 128: the pipelined kernel (one wavefront per SIMD either way); d = 64: the
+  // plain one, which fits two wavefronts per SIMD and hides its latencies with the second
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(256), 0, a.stream, q, k,
+                       v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N, c,
+                       fabsf(a.scale), qxor, qand);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(256), 0, a.stream, q, k, v,
+                       dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N, c,
+                       fabsf(a.scale), qxor, qand);
   return hipGetLastError();
 }
 

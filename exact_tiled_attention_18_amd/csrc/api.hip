@@ -22,8 +22,9 @@ int shape_status(int64_t B, int64_t H, int64_t N, int64_t d, int64_t* count) {
   if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &bhn) || !mul_ok(bhn, d, &n)) return FA_ERR_SHAPE;
   // per-head byte offsets are 32-bit in the kernels: N * d * 4 (fp32) must fit
   if (d > 0 && N > INT32_MAX / (4 * d)) return FA_ERR_SHAPE;
-  // one launch: at most 2^24 workgroups of up to 256 threads
-  if (bh > 0 && (N + 63) / 64 > (int64_t(1) << 24) / bh) return FA_ERR_SHAPE;
+  // one launch: at most 2^32 work-items; the finest grid is the fp32 kernel's, one
+  // workgroup of up to 512 threads per 16 queries
+  if (bh > 0 && (N + 15) / 16 > (int64_t(1) << 23) / bh) return FA_ERR_SHAPE;
   *count = n;
   return FA_OK;
 }

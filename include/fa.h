@@ -51,7 +51,8 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL                        */
   FA_ERR_SHAPE = 2,       /* a negative size, an element count beyond int64,  */
-                          /* or N * d * 4 beyond INT32_MAX (per-head size)     */
+                          /* N * d * 4 beyond INT32_MAX (per-head size), or    */
+                          /* B * H * ceil(N / 16) beyond 2^23 (one launch)     */
   FA_ERR_UNSUPPORTED = 3, /* head dim, dtype, flag or layout not provided      */
   FA_ERR_SCALE = 4,       /* scale is NaN or infinite                          */
   FA_ERR_ALIAS = 5,       /* an output overlaps an input                       */

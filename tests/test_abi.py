@@ -62,6 +62,8 @@ def test_fwd_validation(fa):
     assert _fwd(fa, B=1 << 40, H=1 << 30) == fa.FA_ERR_SHAPE  # element count overflows int64
     # one head's fp32 bytes N * d * 4 must fit the kernels' 32-bit offsets
     assert _fwd(fa, N=(2 ** 31 - 1) // (4 * 64) + 1) == fa.FA_ERR_SHAPE
+    # one launch holds at most 2^32 work-items: B*H*ceil(N/16) workgroups of up to 512 threads
+    assert _fwd(fa, B=1 << 10, H=1 << 10, N=160) == fa.FA_ERR_SHAPE
     assert fa.vt_cols(1) == 64 and fa.vt_cols(64) == 64 and fa.vt_cols(65) == 128
     assert _fwd(fa, d=96) == fa.FA_ERR_UNSUPPORTED
     assert _fwd(fa, dtype=7) == fa.FA_ERR_UNSUPPORTED

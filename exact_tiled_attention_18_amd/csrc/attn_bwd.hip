@@ -25,11 +25,10 @@
 //              out as B operands of dV^T += dO^T P and dK^T += Q^T dS.
 // Tiles are double-buffered: the next tile is loaded into registers while the
 // current one is used, then written to the other buffer before the step's
-// single barrier.  At d = 128 the dK/dV kernel is software-pipelined instead
-// (four tile buffers; each step interleaves the score MFMAs of the next tile,
-// the gradient MFMAs of the previous one and the vector work of the current
-// one); at d = 64 the plain kernel keeps two wavefronts per SIMD, which hides
-// more than the pipeline does with one.
+// single barrier.  At d = 128 both the dQ and the dK/dV kernel are
+// software-pipelined instead (four tile buffers; each step interleaves the
+// score MFMAs of the next tile, the gradient MFMAs of the previous one and the
+// vector work of the current one); at d = 64 the plain kernels are kept.
 //
 // A negative scale flips every sign bit of Q, a zero scale zeroes Q (the
 // kernels then use the positive multiplier |scale| * log2(e)): dQ = scale *
@@ -240,6 +239,217 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const uint16_t* __restrict_
     __syncthreads();
   }
   if (qi < N) store_rows<D>(dq + base + (size_t)qi * D, acc, dq_mul, g);
+}
+
+// ---------------------------------------------------------------- dQ (d = 128)
+// Software pipeline over key tiles, as in the dK/dV kernel: step t issues the MFMAs
+// of S^T_{t+1} = K_{t+1} Q'^T and dP^T_{t+1} = V_{t+1} dO^T, the MFMAs of
+// dQ^T += K_{t-1}^T dS^T_{t-1}, and the vector work that turns S^T_t, dP^T_t into
+// dS^T_t.  Four K/V buffers hold tiles t-1 .. t+2.  To stay within two wavefronts
+// per SIMD, dO (the B operand of dP^T, the same for every tile) is kept in LDS
+// for the whole workgroup instead of in registers.
+template <int D, bool CAUSAL>
+struct DqPipe {
+  using T = Tile<D>;
+  static constexpr int DK = D / 16, DB = D / 32, NB = 4;
+  static constexpr int EPC = 16 / DK;     // score elements per chunk (2)
+  static constexpr int DS = D * 2 + 16;   // dO row stride (bytes): conflict-free 16-byte row reads
+  static_assert(DK == 2 * DB, "one dQ operand per chunk");
+
+  bf16x8 qf[DK];
+  f32x16 acc[DB];
+  f32x16 st[2], dpt[2];     // S^T and dP^T of tiles t (parity B) and t+1
+  uint32_t dsw[2][8];       // dS^T (bf16 pairs) of tiles t (parity B) and t-1
+  bf16x8 opk[2], opv[2], opd[2], opt[2];  // operands of the next chunk
+  uint4 sk, sv;
+  char* kv;     // K buffers at 0 .. NB-1, V buffers at NB .. 2 NB - 1 (BYTES each)
+  char* dos;    // dO rows of the workgroup's queries, stride DS
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  int N, g, li, qi, qloc, krow, tr_off, ld_off, st_off;
+  bool copier;
+  float c, lse2, dd;
+
+  __device__ __forceinline__ char* kbuf(int b) const { return kv + b * T::BYTES; }
+  __device__ __forceinline__ char* vbuf(int b) const { return kv + (NB + b) * T::BYTES; }
+  __device__ __forceinline__ void load(int t) {
+    if (!copier) return;
+    sk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, ld_off + t * kT * D * 2, 0, 0));
+    sv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, ld_off + t * kT * D * 2, 0, 0));
+  }
+  __device__ __forceinline__ void store(int b) {
+    if (!copier) return;
+    *reinterpret_cast<uint4*>(kbuf(b) + st_off) = sk;
+    *reinterpret_cast<uint4*>(vbuf(b) + st_off) = sv;
+  }
+  __device__ __forceinline__ void read_sdp(int slot, int ch, int bn) {
+    opk[slot] = read_row<D>(kbuf(bn), krow, ch, g);
+    opv[slot] = read_row<D>(vbuf(bn), krow, ch, g);
+    opd[slot] = *reinterpret_cast<const bf16x8*>(dos + qloc * DS + ch * 32 + g * 16);
+  }
+  __device__ __forceinline__ void read_kt(int slot, int ch, int bo) {
+    opt[slot] = read_tr<D>(kbuf(bo), tr_off, ch % DB, ch / DB);
+  }
+  __device__ __forceinline__ bf16x8 word8(const uint32_t (&w)[8], int mm) const {
+    return __builtin_bit_cast(bf16x8, make_uint4(w[4 * mm], w[4 * mm + 1], w[4 * mm + 2], w[4 * mm + 3]));
+  }
+  // dS^T of score elements [e0, e0 + EPC) of tile t (parity B)
+  template <int B>
+  __device__ __forceinline__ void grad_slice(int lim, int e0) {
+#pragma unroll
+    for (int e = e0; e < e0 + EPC; e += 2) {
+      float d2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = e + h;
+        const float pr = row_of_reg(r, g) <= lim ? exp2_fast(fmaf(st[B][r], c, -lse2)) : 0.f;
+        d2[h] = pr * (dpt[B][r] - dd);
+      }
+      dsw[B][e >> 1] = pack_bf16x2(d2[0], d2[1]);
+    }
+  }
+  template <int B>
+  __device__ __forceinline__ void step(int t, int cur, bool more, int qlim) {
+    const int bn = (cur + 1) % NB, bo = (cur + NB - 1) % NB, bw = (cur + 2) % NB;
+    const int lim = qlim - t * kT;  // last visible key of this lane's query, relative to tile t
+    read_sdp(0, 0, bn);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[B ^ 1][r] = dpt[B ^ 1][r] = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {
+      if (ch + 1 < DK) {
+        read_sdp((ch + 1) & 1, ch + 1, bn);
+        read_kt((ch + 1) & 1, ch + 1, bo);
+      } else {
+        read_kt(0, 0, cur);  // the next step's chunk 0: K^T of tile t
+      }
+      const int sl = ch & 1, db = ch % DB, mm = ch / DB;
+      acc[db] = mfma(opt[sl], word8(dsw[B ^ 1], mm), acc[db]);
+      st[B ^ 1] = mfma(opk[sl], qf[ch], st[B ^ 1]);
+      dpt[B ^ 1] = mfma(opv[sl], opd[sl], dpt[B ^ 1]);
+      grad_slice<B>(lim, ch * EPC);
+      if (ch == 1) store(bw);
+      if (ch == 2 && more) load(t + 3);
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // DS reads
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);  // DS writes
+      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // VMEM reads
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  }
+  template <int B>
+  __device__ __forceinline__ void last(int b) {
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {
+      const int db = ch % DB, mm = ch / DB;
+      const bf16x8 a = ch == 0 ? opt[0] : read_tr<D>(kbuf(b), tr_off, db, mm);
+      acc[db] = mfma(a, word8(dsw[B], mm), acc[db]);
+    }
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const uint16_t* __restrict__ dout,
+                                                          const float* __restrict__ lse,
+                                                          const float* __restrict__ delta,
+                                                          uint16_t* __restrict__ dq, int BH, int N, int nQB, float c,
+                                                          float dq_mul, uint32_t qxor, uint32_t qand) {
+  using W = DqPipe<D, CAUSAL>;
+  using T = Tile<D>;
+  constexpr int DK = W::DK, NB = W::NB, kBr = 256;
+  __shared__ __attribute__((aligned(16))) char kv[2 * NB * T::BYTES];
+  __shared__ __attribute__((aligned(16))) char dos[kBr * W::DS];
+
+  W w;
+  const int L = blockIdx.x;
+  const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
+  const int bh = L % BH;
+  const size_t base = (size_t)bh * N * D;
+  const int tid = threadIdx.x, lane = tid & 63;
+  w.g = lane >> 5;
+  w.li = lane & 31;
+  const int q0 = qblk * kBr;
+  w.qloc = (tid >> 6) * 32 + w.li;
+  w.qi = q0 + w.qloc;  // this lane's query
+  w.N = N;
+  w.c = c;
+  w.kv = kv;
+  w.dos = dos;
+  constexpr int kRsrcWord3 = 0x00020000;
+  w.krs = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, N * D * 2, kRsrcWord3);
+  w.vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, N * D * 2, kRsrcWord3);
+  w.copier = tid < T::PIECES;
+  const int prow = (tid % T::PIECES) / (D / 8), pcol = (tid % (D / 8)) * 16;
+  w.ld_off = prow * D * 2 + pcol;
+  w.st_off = prow * T::S + pcol;
+  w.krow = permuted_row(w.li);
+  w.tr_off = tr_offset<D>(lane);
+
+  // this lane's query: Q' fragments in registers, its dO row halves into LDS
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) {
+    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    if (w.qi < N) {
+      a = *reinterpret_cast<const uint4*>(q + base + (size_t)w.qi * D + ks * 16 + w.g * 8);
+      b = *reinterpret_cast<const uint4*>(dout + base + (size_t)w.qi * D + ks * 16 + w.g * 8);
+    }
+    a = make_uint4((a.x ^ qxor) & qand, (a.y ^ qxor) & qand, (a.z ^ qxor) & qand, (a.w ^ qxor) & qand);
+    w.qf[ks] = __builtin_bit_cast(bf16x8, a);
+    *reinterpret_cast<uint4*>(dos + w.qloc * W::DS + ks * 32 + w.g * 16) = b;
+  }
+  w.lse2 = w.qi < N ? lse[(size_t)bh * N + w.qi] * kLog2e : 0.f;
+  w.dd = w.qi < N ? delta[(size_t)bh * N + w.qi] : 0.f;
+#pragma unroll
+  for (int db = 0; db < W::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.acc[db][r] = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
+  const int nT = (kv_end + kT - 1) / kT;
+  const int qlim = CAUSAL ? min(w.qi, N - 1) : N - 1;
+  if (nT > 0) {
+    // prologue: tiles 0 and 1 into buffers 0 and 1; K buffer 3 (tile -1 of the first
+    // step's dQ products) zeroed along with dS^T_{-1}; S^T_0, dP^T_0
+    w.load(0);
+    w.store(0);
+    w.load(1);
+    w.store(1);
+    for (int i = tid; i < T::BYTES / 16; i += 512) *reinterpret_cast<uint4*>(w.kbuf(3) + 16 * i) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w.dsw[1][i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.st[0][r] = w.dpt[0][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      w.st[0] = mfma(read_row<D>(w.kbuf(0), w.krow, ks, w.g), w.qf[ks], w.st[0]);
+      w.dpt[0] = mfma(read_row<D>(w.vbuf(0), w.krow, ks, w.g),
+                      *reinterpret_cast<const bf16x8*>(dos + w.qloc * W::DS + ks * 32 + w.g * 16), w.dpt[0]);
+    }
+    w.load(2);
+    w.read_kt(0, 0, 3);
+    int t = 0;
+    for (; t + 1 < nT; t += 2) {
+      w.template step<0>(t, t % NB, t + 3 < nT, qlim);
+      w.template step<1>(t + 1, (t + 1) % NB, t + 4 < nT, qlim);
+    }
+    if (t < nT) {
+      w.template step<0>(t, t % NB, t + 3 < nT, qlim);
+      w.template last<0>(t % NB);
+    } else {
+      w.template last<1>((t - 1) % NB);
+    }
+  }
+  if (w.qi < N) store_rows<D>(dq + base + (size_t)w.qi * D, w.acc, dq_mul, w.g);
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -654,8 +864,12 @@ hipError_t launch_d(const BwdArgs& a) {
   const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
   const int nQB = (N + 255) / 256;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v, dout,
-                     a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v,
+                       dout, a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v, dout,
+                       a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
   const int nKB = (N + 127) / 128;
   // d = 128: the pipelined kernel (one wavefront per SIMD either way); d = 64: the
   // plain one, which fits two wavefronts per SIMD and hides its latencies with the second

@@ -191,7 +191,7 @@ def merge(o_parts, lse_parts):
     return o, lse
 
 
-def backward(q, k, v, do, causal: bool, scale: float):
+def backward(q, k, v, do, causal: bool, scale: float, o=None):
     """Gradients of attention for [B, H, N, d] inputs and output gradient dO.
 
     With S = scale * Q K^T (masked), P = softmax(S) row by row and O = P V, the
@@ -204,9 +204,13 @@ def backward(q, k, v, do, causal: bool, scale: float):
     This is the quantity the pages' training use needs from the saved LSE
     (FlashAttention-2 wiki page, "Leistung und Effizienz": end-to-end training);
     here it is written from the plain definition, materialising P.
+    With `o` given, D_i = sum_c dO_ic o_ic is taken from that output instead:
+    the backward operation receives the forward's output as an input, and a
+    rounded output (bf16) moves D by the rounding, which then enters dS.
     Returns (dQ, dK, dV) as float64 arrays.
     """
     q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    og = None if o is None else _as_f64(o)
     B, H, N, d = q.shape
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     rows = np.arange(N)
@@ -218,7 +222,7 @@ def backward(q, k, v, do, causal: bool, scale: float):
             p = e / e.sum(axis=1, keepdims=True)
             dv[b, h] = p.T @ do[b, h]
             dp = do[b, h] @ v[b, h].T
-            dd = (p * dp).sum(axis=1, keepdims=True)
+            dd = (p * dp).sum(axis=1, keepdims=True) if og is None else (do[b, h] * og[b, h]).sum(axis=1, keepdims=True)
             ds = p * (dp - dd)
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])

@@ -72,3 +72,37 @@ def test_gradient_invariants(causal):
     dq, dk, dv = A.backward(q, k, v, do, causal, 0.3)
     assert np.abs(dk.sum(axis=2)).max() < 1e-10
     assert np.abs(dv.sum(axis=2) - do.sum(axis=2)).max() < 1e-10
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_given_output_equals_the_definition(causal):
+    """D from the exact output (sum_c dO_ic O_ic) is D from P and dP: the same gradients."""
+    q, k, v, do = _case(40, 8)
+    o, _ = A.reference(q, k, v, causal, 0.3)
+    a = A.backward(q, k, v, do, causal, 0.3)
+    b = A.backward(q, k, v, do, causal, 0.3, o=o)
+    assert all(np.abs(x - y).max() < 1e-12 for x, y in zip(a, b))
+
+
+def test_given_output_moves_only_dq_dk_by_the_closed_form():
+    """Moving row i of the given output by e changes D_i by dO_i . e, hence dS_i by
+    -P_i (dO_i . e): dQ_i by -scale (dO_i . e) P_i K, dK by -scale (dO_i . e) P_i^T q_i,
+    every other row of dQ and all of dV unchanged."""
+    q, k, v, do = _case(12, 5, b=1, h=1)
+    scale, i = 0.4, 7
+    o, _ = A.reference(q, k, v, False, scale)
+    e = RNG.standard_normal(5)
+    o2 = o.copy()
+    o2[0, 0, i] += e
+    dq1, dk1, dv1 = A.backward(q, k, v, do, False, scale, o=o)
+    dq2, dk2, dv2 = A.backward(q, k, v, do, False, scale, o=o2)
+    s = scale * q[0, 0] @ k[0, 0].T
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dd = float(do[0, 0, i] @ e)
+    want_dq = np.zeros_like(dq1[0, 0])
+    want_dq[i] = -scale * dd * (p[i] @ k[0, 0])
+    want_dk = -scale * dd * np.outer(p[i], q[0, 0, i])
+    assert np.abs((dq2 - dq1)[0, 0] - want_dq).max() < 1e-12
+    assert np.abs((dk2 - dk1)[0, 0] - want_dk).max() < 1e-12
+    assert np.abs(dv2 - dv1).max() == 0.0

@@ -201,7 +201,7 @@ struct Attn {
     mx[qb] = a;
   }
   __device__ __forceinline__ void new_shift(int qb) {
-    const float mt = c * fmaxf(mx[qb], xor32(mx[qb]));  // -inf when no key of the tile is visible
+    const float mt = c * max_pair(mx[qb]);  // -inf when no key of the tile is visible
     const float m_new = mt > m[qb] + kRescaleSlack ? mt : m[qb];
     // 0 when m was -inf, exactly 1 when unchanged (also for rows with no visible key yet)
     alpha[qb] = m_new == -kInf ? 1.f : exp2_fast(m[qb] - m_new);
@@ -555,8 +555,8 @@ __global__ __launch_bounds__(QB == 1 && D == 128 ? 512 : 256, D == 128 ? 2 : 3) 
   // ---- epilogue: the single division by the row sum, LSE, stores
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
-    const float lt = s.l[qb] + xor32(s.l[qb]);
-    const float lht = s.lh[qb] + xor32(s.lh[qb]);
+    const float lt = sum_pair(s.l[qb]);
+    const float lht = sum_pair(s.lh[qb]);
     const int qi = s.qw0 + qb * 32 + s.li;
     if (qi < N) {
       if constexpr (PART) {

@@ -30,9 +30,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Value exchange with the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float xor32(float x) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ 32) << 2, __float_as_int(x)));
+// Max / sum of a value and its copy in the lane 32 positions away (the other
+// half of the wave), exchanged in registers with v_permlane32_swap: its two
+// results hold the lane's own value and its partner's, in an order that
+// depends on the half, so only symmetric combinations are taken.
+__device__ __forceinline__ float max_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 }  // namespace fa

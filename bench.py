@@ -238,6 +238,50 @@ def bench_backward(fa, w, dev, args):
     print(json.dumps(rec), flush=True)
 
 
+DECODE = {"B": 4, "H": 16, "Nq": 16, "Nk": 16384, "d": 128, "n_splits": 8, "seed": 1200}
+
+
+def bench_split_kv(fa, dev, args):
+    """One step = a decode-shaped split-KV forward: the last Nq positions of a
+    causal sequence of Nk keys, the keys cut into n_splits ranges, one
+    fa_fwd_split launch for all ranges and one fa_merge.  The work is bound by
+    reading K and V once (the scores are a few GFLOP), so the roofline is HBM:
+    algorithmic bytes = K and V once, Q once, the fp32 partials written and read
+    once, O and LSE written once."""
+    c = DECODE
+    B, H, Nq, Nk, d, n = c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["n_splits"]
+    q = synthetic.draw_qkv(B, H, Nq, d, seed=c["seed"], dtype="bf16")[0].to(dev)
+    _, k, v = synthetic.draw_qkv(B, H, Nk, d, seed=c["seed"] + 1, dtype="bf16")
+    k, v = k.to(dev), v.to(dev)
+    o_parts = torch.empty((n, B, H, Nq, d), dtype=torch.float32, device=dev)
+    lse_parts = torch.empty((n, B, H, Nq), dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    scale = d ** -0.5
+
+    def step():
+        fa.fa_fwd_split(q, k, v, n, Nk - Nq, 0, Nk, True, scale, o_parts=o_parts, lse_parts=lse_parts)
+        fa.fa_merge(o_parts, lse_parts, torch.bfloat16, o=o, lse=lse)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sec = time_loop(step, args.steps)
+    nbytes = (2 * B * H * Nk * d * 2 + B * H * Nq * d * 2 + 2 * n * B * H * Nq * (d + 1) * 4
+              + B * H * Nq * (d * 2 + 4))
+    gbs = nbytes / sec / 1e9
+    eprint(f"split-KV decode B{B} H{H} Nq{Nq} Nk{Nk} d{d} x{n}: {sec * 1e6:.1f} us = {gbs:.0f} GB/s "
+           f"= {gbs / HBM_GBPS:.1%} of {HBM_GBPS:.0f} GB/s")
+    rec = {"metric": "split-KV decode GB/s (K, V read once) at 1 MI355X", "value": round(gbs, 1), "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"split_kv_decode_b{B}h{H}nq{Nq}nk{Nk}d{d}x{n}", "causal": True,
+                      "bytes_per_step": nbytes},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBPS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_GBPS, 4), "traffic": None},
+           "cpu_baseline": None}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +293,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fa_bwd) of a bf16 workload instead of the forward")
+    ap.add_argument("--split-kv", action="store_true",
+                    help="time a decode-shaped split-KV forward (fa_fwd_partial per key range + fa_merge)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -274,6 +320,9 @@ def main():
     w = synthetic.workload(args.workload)
     if args.copy_calibration_mib > 0:
         copy_calibration(args.copy_calibration_mib, dev)
+    if args.split_kv:
+        bench_split_kv(fa, dev, args)
+        return
     if args.backward:
         return bench_backward(fa, w, dev, args)
     step, parts = make_step(fa, w, dev)

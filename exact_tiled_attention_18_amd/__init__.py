@@ -57,6 +57,8 @@ def load_library():
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, f32, vp]
     lib.fa_fwd_partial.restype = i32
     lib.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
+    lib.fa_fwd_split.restype = i32
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_bwd.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_merge.restype = i32
@@ -201,6 +203,32 @@ def fa_fwd_partial(q, k, v, q_pos0: int, k_begin: int, k_end: int, causal: bool 
     return o_part, lse_part
 
 
+def fa_fwd_split(q, k, v, n_splits: int, q_pos0: int, k_begin: int, k_end: int, causal: bool = False,
+                 scale: float | None = None, o_parts=None, lse_parts=None, stream=None):
+    """fa_fwd_partial over n_splits consecutive ranges of [k_begin, k_end) in one launch:
+    float32 o_parts [n_splits, B, H, Nq, d] and lse_parts [n_splits, B, H, Nq]; range s is
+    [k_begin + (k_end - k_begin) * s // n_splits, k_begin + (k_end - k_begin) * (s + 1) // n_splits)."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    if o_parts is None:
+        o_parts = torch.empty((n_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_parts is None:
+        lse_parts = torch.empty((n_splits, B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_dense(q, k, v, o_parts, lse_parts)
+    _expect(q, (B, H, Nq, d), torch.bfloat16, "q")
+    _expect(k, (B, H, Nk, d), torch.bfloat16, "k")
+    _expect(v, (B, H, Nk, d), torch.bfloat16, "v")
+    _expect(o_parts, (n_splits, B, H, Nq, d), torch.float32, "o_parts")
+    _expect(lse_parts, (n_splits, B, H, Nq), torch.float32, "lse_parts")
+    lib = load_library()
+    _check(lib.fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o_parts), _ptr(lse_parts), B, H, Nq, Nk, d,
+                            int(q_pos0), int(k_begin), int(k_end), int(n_splits), int(causal), float(scale), FA_BF16,
+                            _stream(stream)))
+    return o_parts, lse_parts
+
+
 def fa_merge(o_parts, lse_parts, dtype=torch.bfloat16, o=None, lse=None, stream=None):
     """O [B, H, N, d] (dtype) and LSE [B, H, N] over the union of the key ranges of
     o_parts (float32 [n, B, H, N, d]) and lse_parts (float32 [n, B, H, N])."""
@@ -222,19 +250,14 @@ def fa_merge(o_parts, lse_parts, dtype=torch.bfloat16, o=None, lse=None, stream=
 
 def split_kv_attention(q, k, v, n_splits: int, causal: bool = False, scale: float | None = None,
                        q_pos0: int | None = None, stream=None):
-    """Split-KV forward: the keys [0, Nk) cut into n_splits contiguous ranges, one
-    fa_fwd_partial call per range into one buffer, then fa_merge.  By default the
-    queries are the last Nq positions of the key sequence (q_pos0 = Nk - Nq)."""
+    """Split-KV forward: the keys [0, Nk) cut into n_splits contiguous ranges, all
+    computed by one fa_fwd_split launch, then fa_merge.  By default the queries are
+    the last Nq positions of the key sequence (q_pos0 = Nk - Nq)."""
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if q_pos0 is None:
         q_pos0 = Nk - Nq
-    o_parts = torch.empty((n_splits, B, H, Nq, d), dtype=torch.float32, device=q.device)
-    lse_parts = torch.empty((n_splits, B, H, Nq), dtype=torch.float32, device=q.device)
-    bounds = [Nk * i // n_splits for i in range(n_splits + 1)]
-    for i in range(n_splits):
-        fa_fwd_partial(q, k, v, q_pos0, bounds[i], bounds[i + 1], causal, scale, o_part=o_parts[i],
-                       lse_part=lse_parts[i], stream=stream)
+    o_parts, lse_parts = fa_fwd_split(q, k, v, n_splits, q_pos0, 0, Nk, causal, scale, stream=stream)
     return fa_merge(o_parts, lse_parts, q.dtype, stream=stream)
 
 

@@ -125,13 +125,14 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const fl
   return hip_status(fa::launch_attn_fp8(a));
 }
 
-int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int64_t B,
-                   int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t q_pos0, int64_t k_begin, int64_t k_end,
-                   int causal, float scale, int dtype, void* stream) {
-  int64_t nq = 0, nk = 0;
+int fa_fwd_split(const void* q, const void* k, const void* v, float* o_parts, float* lse_parts, int64_t B,
+                 int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t q_pos0, int64_t k_begin, int64_t k_end,
+                 int64_t n_splits, int causal, float scale, int dtype, void* stream) {
+  int64_t nq = 0, nk = 0, tot = 0;
   if (int st = shape_status(B, H, Nq, d, &nq)) return st;
   if (int st = shape_status(B, H, Nk, d, &nk)) return st;
   if (k_begin < 0 || k_end < k_begin || k_end > Nk) return FA_ERR_SHAPE;
+  if (n_splits < 1 || n_splits > 65535 || !mul_ok(nq, n_splits, &tot)) return FA_ERR_SHAPE;
   // relative positions (q_pos0 + i - k_begin) must fit the kernels' 32-bit arithmetic
   if (q_pos0 < 0 || q_pos0 > INT32_MAX / 2 - Nq) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -139,17 +140,24 @@ int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, f
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   if (nq == 0) return FA_OK;
-  if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16) || !aligned(lse_part, 4))
+  if (!q || !k || !v || !o_parts || !lse_parts) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_parts, 16) || !aligned(lse_parts, 4))
     return FA_ERR_UNSUPPORTED;
-  const int64_t qb = 2 * nq, kb = 2 * nk, ob = 4 * nq, lb = B * H * Nq * 4;
-  if (overlaps(o_part, ob, q, qb) || overlaps(o_part, ob, k, kb) || overlaps(o_part, ob, v, kb) ||
-      overlaps(lse_part, lb, q, qb) || overlaps(lse_part, lb, k, kb) || overlaps(lse_part, lb, v, kb) ||
-      overlaps(o_part, ob, lse_part, lb))
+  const int64_t qb = 2 * nq, kb = 2 * nk, ob = 4 * tot, lb = B * H * Nq * 4 * n_splits;
+  if (overlaps(o_parts, ob, q, qb) || overlaps(o_parts, ob, k, kb) || overlaps(o_parts, ob, v, kb) ||
+      overlaps(lse_parts, lb, q, qb) || overlaps(lse_parts, lb, k, kb) || overlaps(lse_parts, lb, v, kb) ||
+      overlaps(o_parts, ob, lse_parts, lb))
     return FA_ERR_ALIAS;
-  const fa::AttnArgs a{q, k, v, o_part, lse_part, B, H, Nq, d, causal, scale, static_cast<hipStream_t>(stream)};
-  const fa::PartialArgs p{Nk, q_pos0, k_begin, k_end};
+  const fa::AttnArgs a{q, k, v, o_parts, lse_parts, B, H, Nq, d, causal, scale, static_cast<hipStream_t>(stream)};
+  const fa::PartialArgs p{Nk, q_pos0, k_begin, k_end, n_splits};
   return hip_status(fa::launch_attn_bf16_partial(a, p));
+}
+
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int64_t B,
+                   int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t q_pos0, int64_t k_begin, int64_t k_end,
+                   int causal, float scale, int dtype, void* stream) {
+  return fa_fwd_split(q, k, v, o_part, lse_part, B, H, Nq, Nk, d, q_pos0, k_begin, k_end, 1, causal, scale, dtype,
+                      stream);
 }
 
 int fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse, int64_t B,

@@ -376,6 +376,7 @@ struct Attn {
 // The plain forward has nq = nk = kn = N, k0 = qpos = 0.
 struct Geom {
   int nq, nk, k0, kn, qpos;
+  int nsplit;  // PART: grid row s takes the s-th of nsplit consecutive sub-ranges of [k0, k0 + kn)
 };
 
 // PART: partial result over a key range -- O in fp32 (normalised over the range)
@@ -391,6 +392,16 @@ __global__ __launch_bounds__(QB == 1 && D == 128 ? 512 : 256, D == 128 ? 2 : 3) 
   __shared__ __attribute__((aligned(16))) char smem[Ly::BYTES];
 
   A s;
+  if constexpr (PART) {
+    // sub-range s of the keys, and slice s of the partial outputs
+    const int sp = blockIdx.y;
+    const int b0 = (int)((int64_t)gm.kn * sp / gm.nsplit), b1 = (int)((int64_t)gm.kn * (sp + 1) / gm.nsplit);
+    gm.k0 += b0;
+    gm.qpos -= b0;
+    gm.kn = b1 - b0;
+    o = static_cast<float*>(o) + (size_t)sp * BH * gm.nq * D;
+    lse += (size_t)sp * BH * gm.nq;
+  }
   // work item -> (query block, head): heaviest causal blocks first; consecutive
   // ids go to different XCDs, so with B*H a multiple of 8 all blocks of a head
   // share one XCD's L2
@@ -600,7 +611,8 @@ hipError_t launch(const AttnArgs& a, const Geom& gm) {
   const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
   const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB, PART>), dim3((unsigned)(nQB * BH)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB, PART>), dim3((unsigned)(nQB * BH), (unsigned)gm.nsplit),
+                     dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.o, a.lse, BH, gm, nQB, c, qxor, qand);
   return hipGetLastError();
@@ -617,11 +629,12 @@ hipError_t dispatch(const AttnArgs& a, const Geom& gm) {
 
 hipError_t launch_attn_bf16(const AttnArgs& a) {
   const int n = (int)a.N;
-  return dispatch<false>(a, Geom{n, n, 0, n, 0});
+  return dispatch<false>(a, Geom{n, n, 0, n, 0, 1});
 }
 
 hipError_t launch_attn_bf16_partial(const AttnArgs& a, const PartialArgs& p) {
-  const Geom gm{(int)a.N, (int)p.nk, (int)p.k_begin, (int)(p.k_end - p.k_begin), (int)(p.q_pos0 - p.k_begin)};
+  const Geom gm{(int)a.N, (int)p.nk, (int)p.k_begin, (int)(p.k_end - p.k_begin), (int)(p.q_pos0 - p.k_begin),
+                (int)p.n_splits};
   return dispatch<true>(a, gm);
 }
 

@@ -29,6 +29,7 @@ struct PartialArgs {
   int64_t q_pos0;   // key position of query 0
   int64_t k_begin;  // first key used
   int64_t k_end;    // one past the last key used
+  int64_t n_splits; // consecutive sub-ranges of [k_begin, k_end), one grid row each
 };
 hipError_t launch_attn_bf16_partial(const AttnArgs& a, const PartialArgs& p);
 

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 /* Row length (keys) of transposed V codes: N rounded up to a multiple of 64. */
 #define FA_FP8_VT_COLS(N) ((((N) + 63) / 64) * 64)
@@ -160,6 +160,22 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
 int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t q_pos0,
                    int64_t k_begin, int64_t k_end, int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_split -- fa_fwd_partial over n_splits consecutive key ranges in one
+ * launch, so that short query blocks (decode) still fill the device: range s
+ * (0 <= s < n_splits) is [k_begin + floor((k_end - k_begin) * s / n_splits),
+ * k_begin + floor((k_end - k_begin) * (s + 1) / n_splits)).
+ *   o_parts   : float32 [n_splits, B, H, Nq, d];  lse_parts: float32 [n_splits, B, H, Nq]:
+ *               slice s as fa_fwd_partial writes it for range s (ready for fa_merge).
+ *   1 <= n_splits <= 65535; all other arguments as for fa_fwd_partial.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, dtype, causal),
+ * FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP.
+ */
+int fa_fwd_split(const void* q, const void* k, const void* v, float* o_parts, float* lse_parts,
+                 int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t q_pos0,
+                 int64_t k_begin, int64_t k_end, int64_t n_splits, int causal, float scale, int dtype,
+                 void* stream);
 
 /*
  * fa_merge -- O and LSE over the union of n_parts disjoint key ranges from

@@ -29,7 +29,7 @@ def fa():
 
 def test_header_declares_the_api():
     assert _declared_functions() == ["fa_abi_version", "fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_partial",
-                                     "fa_merge", "fa_quant_rotate_fp8", "fa_status_string"]
+                                     "fa_fwd_split", "fa_merge", "fa_quant_rotate_fp8", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(fa):
 
 
 def test_version_and_status_strings(fa):
-    assert fa.fa_abi_version() == 2
+    assert fa.fa_abi_version() == 3
     assert fa.fa_status_string(0) == "ok"
     assert fa.fa_status_string(3) == "unsupported argument"
     assert fa.fa_status_string(99) == "unknown status"
@@ -134,6 +134,26 @@ def test_partial_validation(fa):
     assert _partial(fa, o=None) == fa.FA_ERR_NULL
     assert _partial(fa, o=ctypes.c_void_p(0x10000 + 32)) == fa.FA_ERR_ALIAS  # o_part overlaps q
     assert _partial(fa, q=None, k=None, v=None, o=None, lse=None, Nq=0) == fa.FA_OK
+
+
+def _split(fa, q=P, k=P2, v=P3, o=P4, lse=P5, B=1, H=1, Nq=64, Nk=128, d=64, pos0=0, kb=0, ke=128, n=4, causal=1,
+           scale=0.125, dtype=1):
+    return fa.load_library().fa_fwd_split(q, k, v, o, lse, B, H, Nq, Nk, d, pos0, kb, ke, n, causal, scale, dtype,
+                                          None)
+
+
+def test_split_validation(fa):
+    assert _split(fa, n=0) == fa.FA_ERR_SHAPE
+    assert _split(fa, n=65536) == fa.FA_ERR_SHAPE              # one grid row per range
+    assert _split(fa, kb=50, ke=40) == fa.FA_ERR_SHAPE
+    assert _split(fa, pos0=2 ** 30) == fa.FA_ERR_SHAPE
+    assert _split(fa, dtype=0) == fa.FA_ERR_UNSUPPORTED
+    assert _split(fa, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert _split(fa, scale=float("inf")) == fa.FA_ERR_SCALE
+    assert _split(fa, lse=None) == fa.FA_ERR_NULL
+    # the n slices of o_parts reach past q's start: overlap detected over all of them
+    assert _split(fa, o=ctypes.c_void_p(0x10000 - 3 * 64 * 64 * 4)) == fa.FA_ERR_ALIAS
+    assert _split(fa, q=None, k=None, v=None, o=None, lse=None, Nq=0) == fa.FA_OK
 
 
 def _merge(fa, op=P, lp=P2, n=3, o=P3, lse=P4, B=1, H=1, N=64, d=64, dtype=1):

@@ -1,7 +1,7 @@
 """GPU parity of the split-KV path: fa_fwd_partial and fa_merge against the oracle.
 
 fa_fwd_partial runs the bf16 forward kernel on one key range with queries at an
-offset position; its O is fp32 but the probabilities feeding P V are rounded to
+offset position (fa_fwd_split on several consecutive ranges in one launch); its O is fp32 but the probabilities feeding P V are rounded to
 bf16 as in fa_fwd, so O carries the bf16 bound (2e-2) and LSE the 1e-3 one.
 Rows that see no key of the range must come back exactly O = 0, LSE = -inf.
 fa_merge is pure fp32 arithmetic: O within 1e-5 (fp32 output; bf16 output
@@ -56,6 +56,43 @@ def test_partial(fa, case):
     eo = np.abs(o[live] - o_ref[live]).max() if live.any() else 0.0
     el = np.abs(lse[live] - l_ref[live]).max() if live.any() else 0.0
     G.log(f"  max|dO| {eo:.3e}  max|dLSE| {el:.3e}  empty rows {int(empty.sum())}")
+    assert eo <= TOL_O and el <= TOL_L
+
+
+# (Nq, Nk, q_pos0, k_begin, k_end, n_splits, causal, d)
+SPLIT_CASES = [
+    (16, 4096, 4080, 0, 4096, 8, True, 128),   # decode: the last 16 positions, 8 ranges
+    (16, 1000, 984, 0, 1000, 7, True, 64),     # ragged ranges
+    (300, 700, 400, 100, 650, 3, True, 128),
+    (64, 100, 0, 0, 100, 16, False, 128),      # ranges of 6 or 7 keys
+    (32, 600, 0, 500, 600, 4, True, 64),       # nothing visible in any range
+    (8, 20, 12, 0, 20, 40, True, 128),         # more ranges than keys: empty ranges
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: "q{}k{}p{}r{}-{}x{}{}d{}".format(
+    c[0], c[1], c[2], c[3], c[4], c[5], "c" if c[6] else "", c[7]))
+def test_split_ranges_in_one_launch(fa, case):
+    """fa_fwd_split: slice s equals the oracle's partial over the s-th range."""
+    nq, nk, pos0, kb, ke, n, causal, d = case
+    G.log(f"case split {case}")
+    q, k, v = _inputs(nq, nk, d, seed=nq + nk + n)
+    scale = d ** -0.5
+    op, lp = fa.fa_fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), n, pos0, kb, ke, causal, scale)
+    torch.cuda.synchronize()
+    op, lp = op.cpu().numpy().astype(np.float64), lp.cpu().numpy().astype(np.float64)
+    eo = el = 0.0
+    for s in range(n):
+        b0, b1 = kb + (ke - kb) * s // n, kb + (ke - kb) * (s + 1) // n
+        o_ref, l_ref = A.partial(q, k, v, causal, scale, pos0, b0, b1)
+        empty = ~np.isfinite(l_ref)
+        assert np.array_equal(~np.isfinite(lp[s]), empty), s
+        assert np.all(lp[s][empty] == -np.inf) and not op[s][empty].any(), s
+        live = ~empty
+        if live.any():
+            eo = max(eo, float(np.abs(op[s][live] - o_ref[live]).max()))
+            el = max(el, float(np.abs(lp[s][live] - l_ref[live]).max()))
+    G.log(f"  max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
     assert eo <= TOL_O and el <= TOL_L
 
 

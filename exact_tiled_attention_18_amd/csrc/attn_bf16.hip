@@ -112,10 +112,10 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
 // whose barriers are independent), which measured 9 % faster non-causal and
 // 28 % faster causal than one 8-wavefront workgroup.  QB = 2: 4 wavefronts, one
 // per SIMD, each with the whole register file, 256 queries.
-template <int D, bool CAUSAL, int QB>
+template <int D, bool CAUSAL, int QB, int WAVES>
 struct Attn {
   static constexpr int kQB = QB;
-  static constexpr int kWaves = QB == 1 && D == 128 ? 8 : 4;
+  static constexpr int kWaves = WAVES;
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kW = 32 * kQB;
   static constexpr int kBr = kWaves * kW;
@@ -381,12 +381,12 @@ struct Geom {
 
 // PART: partial result over a key range -- O in fp32 (normalised over the range)
 // and rows that see no key written as O = 0, LSE = -inf.
-template <int D, bool CAUSAL, int QB, bool PART>
-__global__ __launch_bounds__(QB == 1 && D == 128 ? 512 : 256, D == 128 ? 2 : 3) void attn_fwd_bf16_kernel(
+template <int D, bool CAUSAL, int QB, bool PART, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     void* __restrict__ o, float* __restrict__ lse, int BH, Geom gm, int nQB, float c, uint32_t qxor,
     uint32_t qand) {
-  using A = Attn<D, CAUSAL, QB>;
+  using A = Attn<D, CAUSAL, QB, WAVES>;
   using Ly = typename A::Ly;
   constexpr int DK = A::DK, DB = A::DB, kQB = A::kQB, kW = A::kW, kBr = A::kBr, kThreads = A::kThreads;
   __shared__ __attribute__((aligned(16))) char smem[Ly::BYTES];
@@ -600,10 +600,10 @@ __global__ __launch_bounds__(QB == 1 && D == 128 ? 512 : 256, D == 128 ? 2 : 3) 
   }
 }
 
-template <int D, bool CAUSAL, int QB, bool PART>
+template <int D, bool CAUSAL, int QB, bool PART, int WAVES>
 hipError_t launch(const AttnArgs& a, const Geom& gm) {
-  constexpr int kBr = Attn<D, CAUSAL, QB>::kBr;
-  constexpr int kThreads = Attn<D, CAUSAL, QB>::kThreads;
+  constexpr int kBr = Attn<D, CAUSAL, QB, WAVES>::kBr;
+  constexpr int kThreads = Attn<D, CAUSAL, QB, WAVES>::kThreads;
   const int BH = (int)(a.B * a.H);
   const int nQB = (gm.nq + kBr - 1) / kBr;
   // the kernel needs a positive multiplier c: scale * (q . k) = |scale| * ((-q) . k) for
@@ -611,18 +611,27 @@ hipError_t launch(const AttnArgs& a, const Geom& gm) {
   const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
   const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB, PART>), dim3((unsigned)(nQB * BH), (unsigned)gm.nsplit),
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB, PART, WAVES>), dim3((unsigned)(nQB * BH), (unsigned)gm.nsplit),
                      dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), a.o, a.lse, BH, gm, nQB, c, qxor, qand);
   return hipGetLastError();
 }
 
+// Wavefronts per workgroup (32 queries each with QB = 1): 8 at d = 128, 4 at d = 64
+// (three workgroups per compute unit).  A range of keys for at most 128 queries
+// (decode) takes 4 at d = 128 as well: the workgroup's query block is then mostly
+// empty rows, and smaller workgroups, two per compute unit, waste half as much.
 template <bool PART>
 hipError_t dispatch(const AttnArgs& a, const Geom& gm) {
   constexpr int QB = FA_BF16_QB;
-  if (a.d == 64) return a.causal ? launch<64, true, QB, PART>(a, gm) : launch<64, false, QB, PART>(a, gm);
-  return a.causal ? launch<128, true, QB, PART>(a, gm) : launch<128, false, QB, PART>(a, gm);
+  constexpr int W128 = QB == 1 ? 8 : 4;
+  if (a.d == 64) return a.causal ? launch<64, true, QB, PART, 4>(a, gm) : launch<64, false, QB, PART, 4>(a, gm);
+  if constexpr (PART) {
+    if (gm.nq <= 128)
+      return a.causal ? launch<128, true, QB, PART, 4>(a, gm) : launch<128, false, QB, PART, 4>(a, gm);
+  }
+  return a.causal ? launch<128, true, QB, PART, W128>(a, gm) : launch<128, false, QB, PART, W128>(a, gm);
 }
 
 }  // namespace

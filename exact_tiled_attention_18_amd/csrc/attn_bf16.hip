@@ -521,7 +521,13 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
   };
   // steps with 1 <= t and tiles t, t+1 unmasked need no mask.  Buffer parity
   // B = t % 2 is static: every loop below starts at an odd t and advances by two.
-  const int steady_end = nFull - 1;
+  // the wavefront's own last tile: the last one holding a key visible to one of its
+  // rows (wavefront-uniform; tiles up to nFull - 1 are visible to every row); -1 for
+  // a wavefront whose rows all lie past N (a short last block, decode), which then
+  // only helps with the tile copies
+  int last_w = CAUSAL ? min(gm.qpos + s.qw0 + kW - 1, gm.kn - 1) : gm.kn - 1;
+  last_w = __builtin_amdgcn_readfirstlane(s.qw0 >= N || last_w < 0 ? -1 : last_w / kBc);
+  const int steady_end = min(nFull - 1, last_w + 1);
   s.template step<true, 0>(0, sk_next, sk_w, sv_pv, sv_next, sv_w);
   advance();
   int t = 1;
@@ -531,10 +537,6 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
     s.template step<false, 0>(t + 1, sk_next, sk_w, sv_pv, sv_next, sv_w);
     advance();
   }
-  // the wavefront's own last tile: the last one holding a key visible to one of its
-  // rows (wavefront-uniform; tiles up to nFull - 1 are visible to every row)
-  int last_w = CAUSAL ? min(gm.qpos + s.qw0 + kW - 1, gm.kn - 1) : gm.kn - 1;
-  last_w = __builtin_amdgcn_readfirstlane(last_w >= 0 ? last_w / kBc : -1);
   const int t_end = min(nT, last_w + 1);
   int tn = t;  // next tile
   for (; t < t_end; t += 2) {

@@ -38,8 +38,11 @@ def eprint(*a):
 
 
 def source_sha(name: str) -> str:
-    p = os.path.join(ROOT, "exact_tiled_attention_18_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel's source file together with the device headers it includes."""
+    h = hashlib.sha256()
+    for f in (name, "fa_device.h", "launch.h"):
+        h.update(open(os.path.join(ROOT, "exact_tiled_attention_18_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def hbm_traffic(workload: str, kernel_src: str):
@@ -99,16 +102,16 @@ def _mean_counter(rows, counter: str, pick) -> tuple[float, int]:
     return sum(per_dispatch.values()) / len(per_dispatch), len(per_dispatch)
 
 
-def write_traffic(workload: str, fetch_path: str, write_path: str, copy_mib: int, commands: list[str]) -> dict:
-    """HBM bytes per launch of the attention kernel from two rocprofv3 counter
-    passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
-    same counter reads for the plain copy of copy_mib MiB in the same program."""
-    w = synthetic.workload(workload)
-    attn_tag = {"bf16": "attn_fwd_bf16_kernel", "f32": "attn_fwd_f32_kernel", "fp8": "attn_fwd_fp8_kernel"}[w.dtype]
+def write_traffic(workload: str, attn_tag: str, src: str, algorithmic: float, fetch_path: str, write_path: str,
+                  copy_mib: int, commands: list[str], dst_dir: str | None = None) -> dict:
+    """HBM bytes per launch of the kernel named attn_tag from two rocprofv3
+    counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by
+    what the same counter reads for the plain copy of copy_mib MiB in the same
+    program."""
     is_attn = lambda r: attn_tag in r["Kernel_Name"]  # noqa: E731
     known = float(copy_mib << 20)
     out = {"workload": workload, "kernel": attn_tag,
-           "kernel_source_sha": source_sha(KERNEL_SOURCE[w.dtype]), "copy_bytes": known, "commands": commands}
+           "kernel_source_sha": source_sha(src), "copy_bytes": known, "commands": commands}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
         rows = _counter_rows(path)
@@ -126,8 +129,8 @@ def write_traffic(workload: str, fetch_path: str, write_path: str, copy_mib: int
                         "copy_dispatches": cn, "factor": factor, "bytes_per_launch": kib * 1024.0 * factor}
         total += kib * 1024.0 * factor
     out["bytes_per_launch"] = total
-    out["algorithmic_bytes_per_launch"] = algorithmic_bytes(w)
-    dst = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    out["algorithmic_bytes_per_launch"] = algorithmic
+    dst = os.path.join(dst_dir or os.path.join(ROOT, "profiles"), f"traffic_{workload}.json")
     with open(dst, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
@@ -241,13 +244,28 @@ def bench_backward(fa, w, dev, args):
 DECODE = {"B": 4, "H": 16, "Nq": 16, "Nk": 16384, "d": 128, "n_splits": 8, "seed": 1200}
 
 
+def split_kv_name() -> str:
+    c = DECODE
+    return f"split_kv_decode_b{c['B']}h{c['H']}nq{c['Nq']}nk{c['Nk']}d{c['d']}x{c['n_splits']}"
+
+
+def split_kv_bytes() -> tuple[int, int]:
+    """Algorithmic HBM bytes of the split launch (K and V once, Q once, the fp32
+    partial outputs and LSEs written once) and of the merge (partials read once,
+    O and LSE written once)."""
+    c = DECODE
+    B, H, Nq, Nk, d, n = c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["n_splits"]
+    parts = n * B * H * Nq * (d + 1) * 4
+    return 2 * B * H * Nk * d * 2 + B * H * Nq * d * 2 + parts, parts + B * H * Nq * (d * 2 + 4)
+
+
 def bench_split_kv(fa, dev, args):
     """One step = a decode-shaped split-KV forward: the last Nq positions of a
     causal sequence of Nk keys, the keys cut into n_splits ranges, one
     fa_fwd_split launch for all ranges and one fa_merge.  The work is bound by
-    reading K and V once (the scores are a few GFLOP), so the roofline is HBM:
-    algorithmic bytes = K and V once, Q once, the fp32 partials written and read
-    once, O and LSE written once."""
+    reading K and V once (the scores are a few GFLOP), so the roofline is HBM;
+    value counts the bytes of both launches over the step, the roofline those of
+    the split launch (the dominant kernel) over its own time."""
     c = DECODE
     B, H, Nq, Nk, d, n = c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["n_splits"]
     q = synthetic.draw_qkv(B, H, Nq, d, seed=c["seed"], dtype="bf16")[0].to(dev)
@@ -259,25 +277,35 @@ def bench_split_kv(fa, dev, args):
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
     scale = d ** -0.5
 
-    def step():
+    def split():
         fa.fa_fwd_split(q, k, v, n, Nk - Nq, 0, Nk, True, scale, o_parts=o_parts, lse_parts=lse_parts)
+
+    def merge():
         fa.fa_merge(o_parts, lse_parts, torch.bfloat16, o=o, lse=lse)
+
+    def step():
+        split()
+        merge()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     sec = time_loop(step, args.steps)
-    nbytes = (2 * B * H * Nk * d * 2 + B * H * Nq * d * 2 + 2 * n * B * H * Nq * (d + 1) * 4
-              + B * H * Nq * (d * 2 + 4))
+    k_sec = time_loop(split, args.steps)
+    # the merge alone is shorter than one host call; its share is the step minus the split launch
+    m_sec = sec - k_sec
+    split_bytes, merge_bytes = split_kv_bytes()
+    nbytes = split_bytes + merge_bytes
     gbs = nbytes / sec / 1e9
-    eprint(f"split-KV decode B{B} H{H} Nq{Nq} Nk{Nk} d{d} x{n}: {sec * 1e6:.1f} us = {gbs:.0f} GB/s "
-           f"= {gbs / HBM_GBPS:.1%} of {HBM_GBPS:.0f} GB/s")
+    k_gbs = split_bytes / k_sec / 1e9
+    eprint(f"split-KV decode B{B} H{H} Nq{Nq} Nk{Nk} d{d} x{n}: step {sec * 1e6:.1f} us = {gbs:.0f} GB/s "
+           f"= {gbs / HBM_GBPS:.1%} of {HBM_GBPS:.0f} GB/s; split launch {k_sec * 1e6:.1f} us = {k_gbs:.0f} GB/s "
+           f"= {k_gbs / HBM_GBPS:.1%}; merge (step minus split launch) {m_sec * 1e6:.1f} us")
     rec = {"metric": "split-KV decode GB/s (K, V read once) at 1 MI355X", "value": round(gbs, 1), "unit": "GB/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": f"split_kv_decode_b{B}h{H}nq{Nq}nk{Nk}d{d}x{n}", "causal": True,
-                      "bytes_per_step": nbytes},
-           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBPS, "unit": "GB/s",
-                        "frac": round(gbs / HBM_GBPS, 4), "traffic": None},
+           "config": {"workload": split_kv_name(), "causal": True, "bytes_per_step": nbytes},
+           "roofline": {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_GBPS, "unit": "GB/s",
+                        "frac": round(k_gbs / HBM_GBPS, 4), "traffic": hbm_traffic(split_kv_name(), "attn_bf16.hip")},
            "cpu_baseline": None}
     print(json.dumps(rec), flush=True)
 
@@ -294,7 +322,7 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fa_bwd) of a bf16 workload instead of the forward")
     ap.add_argument("--split-kv", action="store_true",
-                    help="time a decode-shaped split-KV forward (fa_fwd_partial per key range + fa_merge)")
+                    help="time a decode-shaped split-KV forward (one fa_fwd_split launch + fa_merge)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -305,7 +333,13 @@ def main():
     if args.traffic_from:
         if args.copy_calibration_mib <= 0:
             raise SystemExit("--traffic-from needs --copy-calibration-mib (the size the counter runs copied)")
-        rec = write_traffic(args.workload, *args.traffic_from, args.copy_calibration_mib, args.traffic_command)
+        if args.split_kv:
+            name, tag, src, alg = split_kv_name(), "attn_fwd_bf16_kernel", "attn_bf16.hip", split_kv_bytes()[0]
+        else:
+            w = synthetic.workload(args.workload)
+            name, src, alg = w.name, KERNEL_SOURCE[w.dtype], algorithmic_bytes(w)
+            tag = {"bf16": "attn_fwd_bf16_kernel", "f32": "attn_fwd_f32_kernel", "fp8": "attn_fwd_fp8_kernel"}[w.dtype]
+        rec = write_traffic(name, tag, src, alg, *args.traffic_from, args.copy_calibration_mib, args.traffic_command)
         print(json.dumps(rec), flush=True)
         return
     if args.gpus != 1:

@@ -602,32 +602,278 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
   }
 }
 
+// The kernels need a positive multiplier c: scale * (q . k) = |scale| * ((-q) . k) for
+// scale < 0 (negating bf16 is exact), and a zero scale is the same as zero queries.
+struct ScaleArgs {
+  float c;
+  uint32_t qxor, qand;
+};
+inline ScaleArgs scale_args(float scale) {
+  return ScaleArgs{scale == 0.f ? 1.f : fabsf(scale) * kLog2e, scale < 0.f ? 0x80008000u : 0u,
+                   scale == 0.f ? 0u : 0xFFFFFFFFu};
+}
+
 template <int D, bool CAUSAL, int QB, bool PART, int WAVES>
 hipError_t launch(const AttnArgs& a, const Geom& gm) {
   constexpr int kBr = Attn<D, CAUSAL, QB, WAVES>::kBr;
   constexpr int kThreads = Attn<D, CAUSAL, QB, WAVES>::kThreads;
   const int BH = (int)(a.B * a.H);
   const int nQB = (gm.nq + kBr - 1) / kBr;
-  // the kernel needs a positive multiplier c: scale * (q . k) = |scale| * ((-q) . k) for
-  // scale < 0 (negating bf16 is exact), and a zero scale is the same as zero queries
-  const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
-  const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
-  const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
+  const ScaleArgs sc = scale_args(a.scale);
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, QB, PART, WAVES>), dim3((unsigned)(nQB * BH), (unsigned)gm.nsplit),
                      dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), a.o, a.lse, BH, gm, nQB, c, qxor, qand);
+                     static_cast<const uint16_t*>(a.v), a.o, a.lse, BH, gm, nQB, sc.c, sc.qxor, sc.qand);
+  return hipGetLastError();
+}
+
+// ---- split-KV decode: at most 32 queries against each key range of a split
+// launch.  The general kernel gives every 32 queries a wavefront and shares each
+// tile between them, so with one query block a single wavefront per workgroup
+// computes and the range streams at its pace.  Here the workgroup's four
+// wavefronts hold the same queries and take every fourth 32-key tile of the
+// range, each with its own shift, sums and unnormalised output; the four parts
+// are combined through LDS at the end by the same rule as parts over key ranges
+// (scale each by exp2 of its shift minus the largest, then add).  No tile is
+// shared, so K goes from HBM straight into the A-operand registers, one tile
+// ahead; V goes through two LDS slots of the wavefront's own for the
+// transposing read (a wavefront's LDS accesses take effect in issue order, so
+// no barrier is needed until the final combination).
+template <int D>
+struct Decode {
+  static constexpr int kWaves = 4;
+  static constexpr int DK = D / 16, DB = D / 32;
+  static constexpr int VS = D * 2 + 64;                     // V row stride (bytes), as in the general kernel
+  static constexpr int VSLOT = kBc * VS;
+  static constexpr int PIECES = kBc * D * 2 / 16 / 64;      // 16-byte pieces of a V tile per lane
+  static constexpr int kRowsPerPiece = 64 / (D / 8);        // rows between a lane's pieces
+  static constexpr int OS = D + 4;                          // row stride (floats) of a part's O^T
+  static constexpr int PART_FLOATS = 32 * OS + 3 * 32;      // O^T, then shift, l and lh per query
+  static constexpr int SLOTS_BYTES = kWaves * 2 * VSLOT;
+  static constexpr int MERGE_BYTES = kWaves * PART_FLOATS * 4;
+  static constexpr int BYTES = SLOTS_BYTES > MERGE_BYTES ? SLOTS_BYTES : MERGE_BYTES;
+  static_assert(DB <= kWaves, "one d-block of the combination per wavefront");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, D == 128 ? 2 : 3) void attn_decode_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int BH, Geom gm, float c, uint32_t qxor, uint32_t qand) {
+  using Dc = Decode<D>;
+  constexpr int DK = Dc::DK, DB = Dc::DB, VS = Dc::VS, PIECES = Dc::PIECES, kWaves = Dc::kWaves;
+  __shared__ __attribute__((aligned(16))) char smem[Dc::BYTES];
+
+  // range sp of the head's keys; slice sp of the partial outputs
+  const int sp = blockIdx.y, bh = blockIdx.x;
+  const int b0 = (int)((int64_t)gm.kn * sp / gm.nsplit), b1 = (int)((int64_t)gm.kn * (sp + 1) / gm.nsplit);
+  const int kn = b1 - b0, qpos = gm.qpos - b0, N = gm.nq;
+  o += ((size_t)sp * BH + bh) * N * D;
+  lse += ((size_t)sp * BH + bh) * N;
+  const size_t kbase = ((size_t)bh * gm.nk + gm.k0 + b0) * D;
+  constexpr int kRsrcWord3 = 0x00020000;  // raw (untyped) buffer access; reads past the range return zeros
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(k + kbase), (short)0, kn * D * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v + kbase), (short)0, kn * D * 2, kRsrcWord3);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int kv_end = CAUSAL ? min(kn, qpos + N) : kn;  // keys past this are visible to no query
+  const int nT = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
+
+  // queries as the B operand (query li, dims 16 ks + 8 g ..), sign-flipped or zeroed for the scale
+  bf16x8 qf[DK];
+#pragma unroll
+  for (int ks = 0; ks < DK; ++ks) {
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (li < N) val = *reinterpret_cast<const uint4*>(q + ((size_t)bh * N + li) * D + ks * 16 + g * 8);
+    val = make_uint4((val.x ^ qxor) & qand, (val.y ^ qxor) & qand, (val.z ^ qxor) & qand, (val.w ^ qxor) & qand);
+    qf[ks] = __builtin_bit_cast(bf16x8, val);
+  }
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m = -kInf, l = 0.f, lh = 0.f;
+
+  // K: this lane's operand row (permuted, as in the general kernel), dims 16 ks + 8 g ..
+  const int krow_off = permuted_row(li) * D * 2 + g * 16;
+  // V: row-major 16-byte pieces into the wavefront's slots; transposing-read offsets
+  const int vrow = lane / (D / 8), vcol = (lane % (D / 8)) * 16;
+  const int grp16 = lane >> 4, l16 = lane & 15;
+  const int vrd_off = (8 * (grp16 >> 1) + (l16 >> 2)) * VS + (16 * (grp16 & 1) + 4 * (l16 & 3)) * 2;
+  char* const vbase = smem + w * 2 * Dc::VSLOT;
+  auto load_k = [&](int t, bf16x8 (&kr)[DK]) {
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks)
+      kr[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, t * kBc * D * 2 + krow_off + ks * 32, 0, 0));
+  };
+  auto load_v = [&](int t, uint4 (&st)[PIECES]) {
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i)
+      st[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (t * kBc + vrow + i * Dc::kRowsPerPiece) * D * 2 + vcol, 0, 0));
+  };
+
+  bf16x8 kc[DK], kx[DK];
+  uint4 vst[PIECES];
+  int t = w;
+  if (t < nT) {
+    load_k(t, kc);
+    load_v(t, vst);
+  }
+#pragma unroll 1
+  for (int it = 0; t < nT; t += kWaves, ++it) {
+    char* const slot = vbase + (it & 1) * Dc::VSLOT;
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i)
+      *reinterpret_cast<uint4*>(slot + (vrow + i * Dc::kRowsPerPiece) * VS + vcol) = vst[i];
+    const bool more = t + kWaves < nT;
+    if (more) {
+      load_k(t + kWaves, kx);
+      load_v(t + kWaves, vst);
+    }
+    // S^T of tile t: lane half g holds keys t*32 + (r & 7) + 8 g + 2 (r & 8) of query li
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) sc = mfma(kc[ks], qf[ks], sc);
+    const int lim = (CAUSAL ? min(qpos + li, kn - 1) : kn - 1) - t * kBc - g * 8;
+    float mx = -kInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if ((r & 7) + (r & 8) * 2 > lim) sc[r] = -kInf;
+      mx = fmaxf(mx, sc[r]);
+    }
+    // online softmax with the lazy shift (moves only when the maximum exceeds it by the slack)
+    const float mt = c * max_pair(mx);
+    const float m_new = mt > m + kRescaleSlack ? mt : m;
+    const float alpha = m_new == -kInf ? 1.f : exp2_fast(m - m_new);
+    m = m_new;
+    const float msub = m_new == -kInf ? 0.f : m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = exp2_fast(fmaf(sc[r], c, -msub));
+      rs += sc[r];
+    }
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float hs = lh * alpha;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint4 wv;
+      wv.x = pack_bf16x2(sc[8 * h + 0], sc[8 * h + 1]);
+      wv.y = pack_bf16x2(sc[8 * h + 2], sc[8 * h + 3]);
+      wv.z = pack_bf16x2(sc[8 * h + 4], sc[8 * h + 5]);
+      wv.w = pack_bf16x2(sc[8 * h + 6], sc[8 * h + 7]);
+      pb[h] = __builtin_bit_cast(bf16x8, wv);
+      hs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), ones, hs, false);
+      hs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), ones, hs, false);
+      hs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), ones, hs, false);
+      hs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), ones, hs, false);
+    }
+    lh = hs;
+    l = l * alpha + rs;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    // O^T += V_t^T P_t^T
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {
+      const int db = ch % DB, mm = ch / DB;
+      const char* pa = slot + vrd_off + (mm * 16) * VS + db * 64;
+      const v4i16 lo = tr_read(pa), hi = tr_read(pa + 4 * VS);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[db] = mfma(a, pb[mm], oacc[db]);
+    }
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) kc[ks] = kx[ks];
+    }
+  }
+
+  // ---- combination of the four parts (LDS reused once every wavefront is done with its slots)
+  __syncthreads();
+  float* const mine = reinterpret_cast<float*>(smem) + w * Dc::PART_FLOATS;
+  {
+    const float lt = sum_pair(l), lht = sum_pair(lh);
+    if (g == 0) {
+      mine[32 * Dc::OS + li] = m;
+      mine[32 * Dc::OS + 32 + li] = lt;
+      mine[32 * Dc::OS + 64 + li] = lht;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        *reinterpret_cast<float4*>(mine + li * Dc::OS + db * 32 + 8 * a4 + 4 * g) =
+            make_float4(oacc[db][4 * a4], oacc[db][4 * a4 + 1], oacc[db][4 * a4 + 2], oacc[db][4 * a4 + 3]);
+  }
+  __syncthreads();
+  if (w < DB && li < N) {  // wavefront w writes dims 32 w .. 32 w + 31 of every query
+    const float* part = reinterpret_cast<const float*>(smem);
+    float mu[kWaves], f[kWaves];
+    float M = -kInf;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) {
+      mu[u] = part[u * Dc::PART_FLOATS + 32 * Dc::OS + li];
+      M = fmaxf(M, mu[u]);
+    }
+    float L = 0.f, LH = 0.f;
+#pragma unroll
+    for (int u = 0; u < kWaves; ++u) {
+      f[u] = mu[u] == -kInf ? 0.f : exp2_fast(mu[u] - M);
+      L += f[u] * part[u * Dc::PART_FLOATS + 32 * Dc::OS + 32 + li];
+      LH += f[u] * part[u * Dc::PART_FLOATS + 32 * Dc::OS + 64 + li];
+    }
+    // a row with no visible key in the range has l = 0: O = 0, LSE = -inf
+    const float inv = LH > 0.f ? 1.f / LH : 0.f;
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int dcol = w * 32 + 8 * a4 + 4 * g;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < kWaves; ++u) {
+        const float4 x = *reinterpret_cast<const float4*>(part + u * Dc::PART_FLOATS + li * Dc::OS + dcol);
+        acc.x = fmaf(f[u], x.x, acc.x);
+        acc.y = fmaf(f[u], x.y, acc.y);
+        acc.z = fmaf(f[u], x.z, acc.z);
+        acc.w = fmaf(f[u], x.w, acc.w);
+      }
+      *reinterpret_cast<float4*>(o + (size_t)li * D + dcol) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (w == 0 && g == 0) lse[li] = L > 0.f ? (M + log2_fast(L)) * kLn2 : -kInf;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_decode(const AttnArgs& a, const Geom& gm) {
+  const int BH = (int)(a.B * a.H);
+  const ScaleArgs sc = scale_args(a.scale);
+  hipLaunchKernelGGL((attn_decode_bf16_kernel<D, CAUSAL>), dim3((unsigned)BH, (unsigned)gm.nsplit), dim3(256), 0,
+                     a.stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<float*>(a.o), a.lse, BH, gm, sc.c, sc.qxor,
+                     sc.qand);
   return hipGetLastError();
 }
 
 // Wavefronts per workgroup (32 queries each with QB = 1): 8 at d = 128, 4 at d = 64
-// (three workgroups per compute unit).  A range of keys for at most 128 queries
-// (decode) takes 4 at d = 128 as well: the workgroup's query block is then mostly
-// empty rows, and smaller workgroups, two per compute unit, waste half as much.
+// (three workgroups per compute unit).  Key ranges for at most 32 queries (decode)
+// go to the decode kernel above; for at most 128 queries d = 128 takes 4 as well:
+// the workgroup's query block is then mostly empty rows, and smaller workgroups,
+// two per compute unit, waste half as much.
 template <bool PART>
 hipError_t dispatch(const AttnArgs& a, const Geom& gm) {
   constexpr int QB = FA_BF16_QB;
   constexpr int W128 = QB == 1 ? 8 : 4;
+  if constexpr (PART) {
+    if (gm.nq <= 32) {
+      if (a.d == 64) return a.causal ? launch_decode<64, true>(a, gm) : launch_decode<64, false>(a, gm);
+      return a.causal ? launch_decode<128, true>(a, gm) : launch_decode<128, false>(a, gm);
+    }
+  }
   if (a.d == 64) return a.causal ? launch<64, true, QB, PART, 4>(a, gm) : launch<64, false, QB, PART, 4>(a, gm);
   if constexpr (PART) {
     if (gm.nq <= 128)

@@ -10,7 +10,8 @@
 // that lets one row be split over key ranges (split-KV) or over devices.
 //
 // One wavefront per row; the kernel reads each partial once and writes O and
-// LSE once -- it is bound by HBM.  Ranges in which a row sees no key carry
+// LSE once, with the loads of a row issued together so that it is bound by
+// HBM rather than by one memory round trip per range.  Ranges in which a row sees no key carry
 // L_s = -inf and contribute nothing; a row that sees no key at all gets
 // O = 0, L = -inf.
 #include "fa_device.h"
@@ -20,7 +21,23 @@ namespace fa {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // wavefronts per workgroup
+constexpr int kUnroll = 8;        // partial rows whose loads are in flight together
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Lane j holds the LSE of range s0 + j, so a row's LSEs arrive in one load per 64
+// ranges and the maximum and the sum of the weights are wave reductions; the
+// partial rows are then read kUnroll at a time, each weighted by its range's
+// factor taken from the lane that holds it.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kRowsPerBlock * 64) void merge_kernel(const float* __restrict__ o_parts,
                                                                    const float* __restrict__ lse_parts, int n,
@@ -28,25 +45,43 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void merge_kernel(const float* 
                                                                    int64_t rows) {
   constexpr int C = D / 64;  // columns per lane
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  if (row >= rows) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
   float mx = -kInf;
-  for (int s = 0; s < n; ++s) mx = fmaxf(mx, lse_parts[(int64_t)s * rows + row]);
+  for (int s0 = 0; s0 < n; s0 += 64)
+    if (s0 + lane < n) mx = fmaxf(mx, lse_parts[(int64_t)(s0 + lane) * rows + row]);
+  mx = wave_max(mx);
   float acc[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) acc[j] = 0.f;
   float sum = 0.f;
   if (mx != -kInf) {
-    for (int s = 0; s < n; ++s) {
-      const float w = exp2_fast((lse_parts[(int64_t)s * rows + row] - mx) * kLog2e);  // exp(-inf) = 0
-      sum += w;
-      const float* src = o_parts + ((int64_t)s * rows + row) * D + lane * C;
-      if constexpr (C == 2) {
-        const float2 x = *reinterpret_cast<const float2*>(src);
-        acc[0] = fmaf(w, x.x, acc[0]);
-        acc[1] = fmaf(w, x.y, acc[1]);
-      } else {
-        acc[0] = fmaf(w, src[0], acc[0]);
+    for (int s0 = 0; s0 < n; s0 += 64) {
+      const int cnt = n - s0 < 64 ? n - s0 : 64;
+      // weight of range s0 + lane: exp(L_s - max), 0 for a range the row does not see
+      const float ws = lane < cnt ? exp2_fast((lse_parts[(int64_t)(s0 + lane) * rows + row] - mx) * kLog2e) : 0.f;
+      sum += wave_sum(ws);
+      for (int j0 = 0; j0 < cnt; j0 += kUnroll) {
+        float x[kUnroll][C];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int s = s0 + (j0 + u < cnt ? j0 + u : cnt - 1);  // in range; the weight of a repeat is 0
+          const float* src = o_parts + ((int64_t)s * rows + row) * D + lane * C;
+          if constexpr (C == 2) {
+            const float2 v2 = *reinterpret_cast<const float2*>(src);
+            x[u][0] = v2.x;
+            x[u][1] = v2.y;
+          } else {
+            x[u][0] = src[0];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int j = j0 + u < cnt ? j0 + u : 0;
+          const float w = j0 + u < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), j)) : 0.f;
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[c] = fmaf(w, x[u][c], acc[c]);
+        }
       }
     }
   }

@@ -1,7 +1,9 @@
 """GPU parity of the split-KV path: fa_fwd_partial and fa_merge against the oracle.
 
 fa_fwd_partial runs the bf16 forward kernel on one key range with queries at an
-offset position (fa_fwd_split on several consecutive ranges in one launch); its O is fp32 but the probabilities feeding P V are rounded to
+offset position (fa_fwd_split on several consecutive ranges in one launch; at
+most 32 queries take the decode kernel, which splits each range over four
+wavefronts); its O is fp32 but the probabilities feeding P V are rounded to
 bf16 as in fa_fwd, so O carries the bf16 bound (2e-2) and LSE the 1e-3 one.
 Rows that see no key of the range must come back exactly O = 0, LSE = -inf.
 fa_merge is pure fp32 arithmetic: O within 1e-5 (fp32 output; bf16 output
@@ -29,6 +31,9 @@ CASES = [
     (100, 333, 0, 17, 333, False, 64),     # ragged range
     (257, 513, 100, 0, 290, True, 128),    # some rows see nothing, others part of the range
     (1, 5000, 4999, 1234, 4999, True, 128),
+    (32, 3000, 0, 0, 3000, False, 128),    # decode kernel, non-causal, 94 tiles over four wavefronts
+    (17, 70, 53, 0, 70, True, 64),         # decode kernel, three tiles: one wavefront has none
+    (33, 900, 867, 0, 900, True, 128),     # one query past the decode kernel's limit
 ]
 
 
@@ -67,6 +72,9 @@ SPLIT_CASES = [
     (64, 100, 0, 0, 100, 16, False, 128),      # ranges of 6 or 7 keys
     (32, 600, 0, 500, 600, 4, True, 64),       # nothing visible in any range
     (8, 20, 12, 0, 20, 40, True, 128),         # more ranges than keys: empty ranges
+    (1, 16384, 16383, 0, 16384, 8, True, 128),  # one new token
+    (32, 2000, 0, 0, 2000, 5, False, 64),
+    (20, 4133, 4113, 0, 4133, 6, True, 128),    # ranges ending mid-tile
 ]
 
 
@@ -96,12 +104,33 @@ def test_split_ranges_in_one_launch(fa, case):
     assert eo <= TOL_O and el <= TOL_L
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9])
+@pytest.mark.parametrize("nq", [16, 100])
+def test_split_scales(fa, scale, nq):
+    """Negative, zero and large scales through both the decode kernel (16 queries)
+    and the general one (100 queries)."""
+    G.log(f"case split scale={scale} nq={nq}")
+    nk, d, n = 1500, 128, 4
+    q, k, v = _inputs(nq, nk, d, seed=4242)
+    op, lp = fa.fa_fwd_split(q.to(DEV), k.to(DEV), v.to(DEV), n, nk - nq, 0, nk, True, scale)
+    torch.cuda.synchronize()
+    op, lp = op.cpu().numpy().astype(np.float64), lp.cpu().numpy().astype(np.float64)
+    for s in range(n):
+        o_ref, l_ref = A.partial(q, k, v, True, scale, nk - nq, nk * s // n, nk * (s + 1) // n)
+        assert np.isfinite(l_ref).all()
+        eo, el = np.abs(op[s] - o_ref).max(), np.abs(lp[s] - l_ref).max()
+        G.log(f"  range {s}: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+        assert eo <= TOL_O and el <= TOL_L
+
+
+@pytest.mark.parametrize("n", [5, 64, 70])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_merge(fa, d, dtype):
-    G.log(f"case merge d={d} {dtype}")
-    rng = np.random.default_rng(d)
-    n, B, H, N = 5, 2, 3, 77
+def test_merge(fa, d, dtype, n):
+    """n = 64 and 70: a row's range LSEs are read 64 at a time (one per lane)."""
+    G.log(f"case merge d={d} {dtype} n={n}")
+    rng = np.random.default_rng(d + n)
+    B, H, N = 2, 3, 77
     o_parts = rng.standard_normal((n, B, H, N, d)).astype(np.float32)
     lse_parts = (3.0 * rng.standard_normal((n, B, H, N))).astype(np.float32)
     lse_parts[rng.random((n, B, H, N)) < 0.3] = -np.inf   # ranges a row does not see

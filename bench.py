@@ -334,7 +334,7 @@ def main():
         if args.copy_calibration_mib <= 0:
             raise SystemExit("--traffic-from needs --copy-calibration-mib (the size the counter runs copied)")
         if args.split_kv:
-            name, tag, src, alg = split_kv_name(), "attn_fwd_bf16_kernel", "attn_bf16.hip", split_kv_bytes()[0]
+            name, tag, src, alg = split_kv_name(), "attn_decode_bf16_kernel", "attn_bf16.hip", split_kv_bytes()[0]
         else:
             w = synthetic.workload(args.workload)
             name, src, alg = w.name, KERNEL_SOURCE[w.dtype], algorithmic_bytes(w)

@@ -162,6 +162,34 @@ def test_split_kv_decode(fa, n_splits):
     assert eo <= TOL_O and el <= TOL_L
 
 
+def test_split_kv_decode_bench_shape(fa):
+    """The split-KV bench's workload (B4 H16, the last 16 of 16384 causal positions,
+    d = 128, 8 ranges) in its launch configuration: fa_fwd_split then fa_merge, with
+    three heads checked against the oracle, each range's partial and the merged row."""
+    import bench
+    c = bench.DECODE
+    B, H, Nq, Nk, d, n = c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["n_splits"]
+    G.log(f"case split-KV decode bench shape {c}")
+    q = synthetic.draw_qkv(B, H, Nq, d, seed=c["seed"], dtype="bf16")[0]
+    _, k, v = synthetic.draw_qkv(B, H, Nk, d, seed=c["seed"] + 1, dtype="bf16")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    scale = d ** -0.5
+    op, lp = fa.fa_fwd_split(qd, kd, vd, n, Nk - Nq, 0, Nk, True, scale)
+    o, lse = fa.fa_merge(op, lp, torch.bfloat16)
+    torch.cuda.synchronize()
+    op, lp = op.cpu().numpy().astype(np.float64), lp.cpu().numpy().astype(np.float64)
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    for b, h in ((0, 0), (1, 7), (3, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        for s in range(n):
+            o_ref, l_ref = A.partial(q[sl], k[sl], v[sl], True, scale, Nk - Nq, Nk * s // n, Nk * (s + 1) // n)
+            assert np.abs(op[s][sl] - o_ref).max() <= TOL_O and np.abs(lp[s][sl] - l_ref).max() <= TOL_L
+        o_ref, l_ref = A.partial(q[sl], k[sl], v[sl], True, scale, Nk - Nq, 0, Nk)
+        eo, el = np.abs(o[sl] - o_ref).max(), np.abs(lse[sl] - l_ref).max()
+        G.log(f"  head ({b},{h}) merged: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+        assert eo <= TOL_O and el <= TOL_L
+
+
 def test_split_kv_square_matches_full_forward(fa):
     """The square causal problem split in four key ranges equals fa_fwd within bf16 rounding."""
     q, k, v = _inputs(1024, 1024, 128, seed=5)

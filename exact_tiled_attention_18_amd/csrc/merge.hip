@@ -36,8 +36,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // Lane j holds the LSE of range s0 + j, so a row's LSEs arrive in one load per 64
 // ranges and the maximum and the sum of the weights are wave reductions; the
-// partial rows are then read kUnroll at a time, each weighted by its range's
-// factor taken from the lane that holds it.
+// partial rows are read kUnroll at a time, each weighted by its range's factor
+// taken from the lane that holds it.  The first batch of partial rows does not
+// depend on the weights and is loaded together with the LSEs, so up to kUnroll
+// ranges cost one memory round trip.
 template <int D, bool BF16>
 __global__ __launch_bounds__(kRowsPerBlock * 64) void merge_kernel(const float* __restrict__ o_parts,
                                                                    const float* __restrict__ lse_parts, int n,
@@ -47,8 +49,28 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void merge_kernel(const float* 
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
-  float mx = -kInf;
-  for (int s0 = 0; s0 < n; s0 += 64)
+  float x[kUnroll][C];
+  // rows s0 + j0 .. s0 + j0 + kUnroll - 1 of the partials (indices past cnt repeat the
+  // last range, whose weight there is 0)
+  auto load_batch = [&](int s0, int j0, int cnt) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int s = s0 + (j0 + u < cnt ? j0 + u : cnt - 1);
+      const float* src = o_parts + ((int64_t)s * rows + row) * D + lane * C;
+      if constexpr (C == 2) {
+        const float2 v2 = *reinterpret_cast<const float2*>(src);
+        x[u][0] = v2.x;
+        x[u][1] = v2.y;
+      } else {
+        x[u][0] = src[0];
+      }
+    }
+  };
+  const int cnt0 = n < 64 ? n : 64;
+  const float ls0 = lane < cnt0 ? lse_parts[(int64_t)lane * rows + row] : -kInf;
+  if (n > 0) load_batch(0, 0, cnt0);
+  float mx = ls0;
+  for (int s0 = 64; s0 < n; s0 += 64)
     if (s0 + lane < n) mx = fmaxf(mx, lse_parts[(int64_t)(s0 + lane) * rows + row]);
   mx = wave_max(mx);
   float acc[C];
@@ -58,23 +80,12 @@ __global__ __launch_bounds__(kRowsPerBlock * 64) void merge_kernel(const float* 
   if (mx != -kInf) {
     for (int s0 = 0; s0 < n; s0 += 64) {
       const int cnt = n - s0 < 64 ? n - s0 : 64;
+      const float ls = s0 == 0 ? ls0 : (lane < cnt ? lse_parts[(int64_t)(s0 + lane) * rows + row] : -kInf);
       // weight of range s0 + lane: exp(L_s - max), 0 for a range the row does not see
-      const float ws = lane < cnt ? exp2_fast((lse_parts[(int64_t)(s0 + lane) * rows + row] - mx) * kLog2e) : 0.f;
+      const float ws = lane < cnt ? exp2_fast((ls - mx) * kLog2e) : 0.f;
       sum += wave_sum(ws);
       for (int j0 = 0; j0 < cnt; j0 += kUnroll) {
-        float x[kUnroll][C];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int s = s0 + (j0 + u < cnt ? j0 + u : cnt - 1);  // in range; the weight of a repeat is 0
-          const float* src = o_parts + ((int64_t)s * rows + row) * D + lane * C;
-          if constexpr (C == 2) {
-            const float2 v2 = *reinterpret_cast<const float2*>(src);
-            x[u][0] = v2.x;
-            x[u][1] = v2.y;
-          } else {
-            x[u][0] = src[0];
-          }
-        }
+        if (s0 > 0 || j0 > 0) load_batch(s0, j0, cnt);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           const int j = j0 + u < cnt ? j0 + u : 0;

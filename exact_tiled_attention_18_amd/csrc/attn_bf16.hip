@@ -588,21 +588,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
         const float inv = 1.f / lht;
         uint16_t* op = static_cast<uint16_t*>(o) + base + (size_t)qi * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            // lane half g holds dims 16j + 4g .. and 16j + 8 + 4g ..: one swap with the
-            // partner lane gives each half 8 consecutive dims, stored as 16 bytes
-            const f32x16& a = s.oacc[db][qb];
-            const int r = 8 * j;
-            const uint32_t ex = pack_bf16x2(a[r + 0] * inv, a[r + 1] * inv);
-            const uint32_t ey = pack_bf16x2(a[r + 2] * inv, a[r + 3] * inv);
-            const uint32_t ox = pack_bf16x2(a[r + 4] * inv, a[r + 5] * inv);
-            const uint32_t oy = pack_bf16x2(a[r + 6] * inv, a[r + 7] * inv);
-            const auto rx = __builtin_amdgcn_permlane32_swap(ex, ox, false, false);
-            const auto ry = __builtin_amdgcn_permlane32_swap(ey, oy, false, false);
-            *reinterpret_cast<uint4*>(op + db * 32 + 16 * j + 8 * s.g) = make_uint4(rx[0], ry[0], rx[1], ry[1]);
-          }
+        for (int db = 0; db < DB; ++db) store_row_bf16(op + db * 32, s.oacc[db][qb], inv, s.g);
         if (s.g == 0) lse[(size_t)bh * N + qi] = (s.m[qb] + log2_fast(lt)) * kLn2;
       }
     }

@@ -99,19 +99,12 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// stores of a transposed 32 x 32 accumulator block: lane (row l % 32) receives
-// columns db * 32 + 8 a4 + 4 g .. +3 of its row
+// stores of transposed 32 x 32 accumulator blocks: lane (row l % 32) receives
+// columns db * 32 .. db * 32 + 31 of its row
 template <int D>
 __device__ __forceinline__ void store_rows(uint16_t* dst_row, const f32x16 (&acc)[D / 32], float mul, int g) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      uint2 w;
-      w.x = pack_bf16x2(acc[db][4 * a4 + 0] * mul, acc[db][4 * a4 + 1] * mul);
-      w.y = pack_bf16x2(acc[db][4 * a4 + 2] * mul, acc[db][4 * a4 + 3] * mul);
-      *reinterpret_cast<uint2*>(dst_row + db * 32 + 8 * a4 + 4 * g) = w;
-    }
+  for (int db = 0; db < D / 32; ++db) store_row_bf16(dst_row + db * 32, acc[db], mul, g);
 }
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)

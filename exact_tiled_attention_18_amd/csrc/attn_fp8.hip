@@ -420,15 +420,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   if (qi < N) {
     const float inv = s.svmax / lt;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int dcol = db * 32 + 8 * a4 + 4 * s.g;
-        uint2 w;
-        w.x = pack_bf16x2(s.oacc[db][4 * a4 + 0] * inv, s.oacc[db][4 * a4 + 1] * inv);
-        w.y = pack_bf16x2(s.oacc[db][4 * a4 + 2] * inv, s.oacc[db][4 * a4 + 3] * inv);
-        *reinterpret_cast<uint2*>(o + base + (size_t)qi * kD + dcol) = w;
-      }
+    for (int db = 0; db < 4; ++db) store_row_bf16(o + base + (size_t)qi * kD + db * 32, s.oacc[db], inv, s.g);
     if (s.g == 0) lse[(size_t)bh * N + qi] = (s.m + log2_fast(lt) - kPShift) * kLn2;
   }
 }

@@ -43,4 +43,23 @@ __device__ __forceinline__ float sum_pair(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Stores one row of a transposed 32x32 accumulator block as bf16 (times mul).  In
+// the accumulator layout lane half g holds dims 8 a4 + 4 g .. + 3 of the lane's
+// row (a4 = 0..3); one swap with the partner lane per pair of such pieces gives
+// each half 8 consecutive dims, stored as 16 bytes at dst + 16 j + 8 g.  Both
+// lanes of a pair hold the same row, so they are active together.
+__device__ __forceinline__ void store_row_bf16(uint16_t* dst, const f32x16& a, float mul, int g) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j;
+    const uint32_t ex = pack_bf16x2(a[r + 0] * mul, a[r + 1] * mul);
+    const uint32_t ey = pack_bf16x2(a[r + 2] * mul, a[r + 3] * mul);
+    const uint32_t ox = pack_bf16x2(a[r + 4] * mul, a[r + 5] * mul);
+    const uint32_t oy = pack_bf16x2(a[r + 6] * mul, a[r + 7] * mul);
+    const auto rx = __builtin_amdgcn_permlane32_swap(ex, ox, false, false);
+    const auto ry = __builtin_amdgcn_permlane32_swap(ey, oy, false, false);
+    *reinterpret_cast<uint4*>(dst + 16 * j + 8 * g) = make_uint4(rx[0], ry[0], rx[1], ry[1]);
+  }
+}
+
 }  // namespace fa

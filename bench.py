@@ -182,6 +182,26 @@ def time_loop(fn, iters: int) -> float:
     return e0.elapsed_time(e1) / 1e3 / iters
 
 
+def warm_up(fn, steps: int, min_s: float) -> tuple[int, float]:
+    """Untimed warm-up: at least `steps` calls of fn, continued until min_s seconds of
+    back-to-back work have passed.  The chip raises its clock over tens of
+    milliseconds of sustained load (a 20-step warm-up of a 100 us step ends well
+    inside that ramp), so timing right after a short warm-up measures the ramp.
+    Returns the number of calls made and the seconds they took."""
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(steps):
+        fn()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
 def cpu_baseline(w, budget_s: float):
     """The fp64 oracle, timed on this host on a bounded sample of the workload's heads."""
     from oracle import attention as A
@@ -222,16 +242,15 @@ def bench_backward(fa, w, dev, args):
 
     def step():
         fa.fa_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, delta=delta)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    wn, ws = warm_up(step, args.warmup, args.min_warmup_s)
     sec = time_loop(step, args.steps)
     flops = 2.5 * w.flops()
     tflops = flops / sec / 1e12
     peak = PEAK_TFLOPS["bf16"]
     eprint(f"{w.name} backward: {sec * 1e6:.1f} us = {tflops:.1f} TFLOP/s = {tflops / peak:.1%} of {peak}")
     rec = {"metric": "attention bwd TFLOP/s at 1 MI355X (2.5x forward FLOPs)", "value": round(tflops, 2),
-           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": wn,
+           "warmup_requested": args.warmup, "warmup_s": round(ws, 3),
            "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic",
            "config": {"workload": w.name, "pass": "backward", "flops_per_step": flops},
@@ -286,9 +305,7 @@ def bench_split_kv(fa, dev, args):
     def step():
         split()
         merge()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    wn, ws = warm_up(step, args.warmup, args.min_warmup_s)
     sec = time_loop(step, args.steps)
     k_sec = time_loop(split, args.steps)
     # the merge alone is shorter than one host call; its share is the step minus the split launch
@@ -301,7 +318,8 @@ def bench_split_kv(fa, dev, args):
            f"= {gbs / HBM_GBPS:.1%} of {HBM_GBPS:.0f} GB/s; split launch {k_sec * 1e6:.1f} us = {k_gbs:.0f} GB/s "
            f"= {k_gbs / HBM_GBPS:.1%}; merge (step minus split launch) {m_sec * 1e6:.1f} us")
     rec = {"metric": "split-KV decode GB/s (K, V read once) at 1 MI355X", "value": round(gbs, 1), "unit": "GB/s",
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5),
+           "n_gpus": 1, "steps": args.steps, "warmup": wn, "warmup_requested": args.warmup,
+           "warmup_s": round(ws, 3), "ms_per_step": round(sec * 1e3, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": split_kv_name(), "causal": True, "bytes_per_step": nbytes},
            "roofline": {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_GBPS, "unit": "GB/s",
@@ -314,7 +332,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20, help="untimed warm-up steps (at least)")
+    ap.add_argument("--min-warmup-s", type=float, default=0.5,
+                    help="keep warming up until this many seconds of back-to-back steps have run "
+                         "(the clock ramps up under sustained load); 'warmup' in the output is the count run")
     ap.add_argument("--workload", default="bf16_causal_b4h16n2048d128",
                     choices=[w.name for w in synthetic.WORKLOADS])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
@@ -360,9 +381,7 @@ def main():
     if args.backward:
         return bench_backward(fa, w, dev, args)
     step, parts = make_step(fa, w, dev)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    wn, ws = warm_up(step, args.warmup, args.min_warmup_s)
 
     t0 = time.perf_counter()
     sec = time_loop(step, args.steps)
@@ -393,7 +412,8 @@ def main():
     rec = {
         "metric": "attention fwd TFLOP/s at 1 MI355X and % of dense MFMA peak (bf16, fp8)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+        "warmup": wn, "warmup_requested": args.warmup, "warmup_s": round(ws, 3),
+        "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "scale": "1/sqrt(d)", "flops_per_step": w.flops()},

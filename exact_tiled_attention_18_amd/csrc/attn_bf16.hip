@@ -211,18 +211,26 @@ struct Attn {
     msub[qb] = m_new == -kInf ? 0.f : m_new;
     rs[qb] = 0.f;
   }
-  __device__ __forceinline__ void exps(int B, int e0, int e1) {
+  // exponentials of scores e0 .. e0 + n - 1 (n a power of two dividing 16, so one
+  // query block), added to the row sum as a pairwise tree (short dependency chains)
+  template <int n>
+  __device__ __forceinline__ void exps(int B, int e0) {
+    const int qb = e0 / 16, r0 = e0 % 16;
+    float t[n];
 #pragma unroll
-    for (int e = e0; e < e1; ++e) {
-      const int qb = e / 16, r = e % 16;
-      const float p = exp2_fast(fmaf(sbuf[B][qb][r], c, -msub[qb]));  // masked: exp2(-inf) = 0
-      sbuf[B][qb][r] = p;
-      rs[qb] += p;
+    for (int i = 0; i < n; ++i) {
+      t[i] = exp2_fast(fmaf(sbuf[B][qb][r0 + i], c, -msub[qb]));  // masked: exp2(-inf) = 0
+      sbuf[B][qb][r0 + i] = t[i];
     }
+#pragma unroll
+    for (int w = n / 2; w >= 1; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) t[i] += t[i + w];
+    rs[qb] += t[0];
   }
   __device__ __forceinline__ void pack(int B, int qb) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float h_acc = lh[qb];
+    float h_acc[2] = {lh[qb], 0.f};  // one dot-product chain per half
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint4 wv;
@@ -231,13 +239,19 @@ struct Attn {
       wv.z = pack_bf16x2(sbuf[B][qb][8 * h + 4], sbuf[B][qb][8 * h + 5]);
       wv.w = pack_bf16x2(sbuf[B][qb][8 * h + 6], sbuf[B][qb][8 * h + 7]);
       pbuf[B][qb][h] = __builtin_bit_cast(bf16x8, wv);
-      h_acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), ones, h_acc, false);
-      h_acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), ones, h_acc, false);
-      h_acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), ones, h_acc, false);
-      h_acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), ones, h_acc, false);
+      h_acc[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), ones, h_acc[h], false);
+      h_acc[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), ones, h_acc[h], false);
+      h_acc[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), ones, h_acc[h], false);
+      h_acc[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), ones, h_acc[h], false);
     }
-    lh[qb] = h_acc;
+    lh[qb] = h_acc[0] + h_acc[1];
     l[qb] += rs[qb];
+    // The probabilities and sums are next read after the step's conditional rescale
+    // of O; without a use here the compiler's IR sinking moves the whole softmax
+    // (exponentials included) past that branch, out of reach of the step's MFMAs.
+    // An empty volatile asm reading them keeps the work in its chunks.
+    const i32x4 p0 = __builtin_bit_cast(i32x4, pbuf[B][qb][0]), p1 = __builtin_bit_cast(i32x4, pbuf[B][qb][1]);
+    asm volatile("" ::"v"(p0), "v"(p1), "v"(lh[qb]), "v"(l[qb]));
   }
   // slice ch of the softmax work: mask and row max, shift, the 16*kQB exponentials
   // spread over the middle chunks, packing at the end
@@ -260,10 +274,8 @@ struct Attn {
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) new_shift(qb);
     }
-    if (ch >= first_exp && ch < last_exp) {
-      const int e0 = (ch - first_exp) * per;
-      exps(B, e0, e0 + per < E ? e0 + per : E);
-    }
+    static_assert(per * (last_exp - first_exp) == E && 16 % per == 0, "whole power-of-two runs of one query block");
+    if (ch >= first_exp && ch < last_exp) exps<per>(B, (ch - first_exp) * per);
     if (ch == NCH - 2) pack(B, 0);
     if (ch == NCH - 1 && kQB == 2) pack(B, 1);
   }

@@ -90,3 +90,30 @@ def test_traffic_from_needs_the_copy_size(tmp_path, flag):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--traffic-from", str(tmp_path),
                         str(tmp_path)] + flag, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and "--copy-calibration-mib" in r.stderr
+
+
+def test_warm_up_runs_at_least_the_steps_and_the_time(monkeypatch):
+    # no GPU here: synchronisation is a no-op, and each "step" advances a fake clock
+    monkeypatch.setattr(bench.torch.cuda, "synchronize", lambda: None)
+    clock = {"t": 0.0}
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: clock["t"])
+    calls = {"n": 0}
+
+    def step(dt):
+        def f():
+            calls["n"] += 1
+            clock["t"] += dt
+        return f
+
+    # long steps: the requested count already covers the minimum time
+    n, s = bench.warm_up(step(0.1), 20, 0.5)
+    assert n == calls["n"] == 20 and s == pytest.approx(2.0)
+    # short steps: the count is topped up, in tens, until the minimum time has passed
+    calls["n"] = 0
+    clock["t"] = 0.0
+    n, s = bench.warm_up(step(1e-4), 20, 0.5)
+    assert n == calls["n"] and n >= 5000 and (n - 20) % 10 == 0 and s >= 0.5
+    # no minimum time: exactly the requested count
+    calls["n"] = 0
+    n, _ = bench.warm_up(step(1e-4), 7, 0.0)
+    assert n == calls["n"] == 7

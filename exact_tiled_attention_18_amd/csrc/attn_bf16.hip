@@ -468,6 +468,13 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
     return;
   }
 
+  // the first tiles' loads go out together, ahead of the Q loads: each would
+  // otherwise wait for its own memory round trip before the next is issued
+  uint4 pro_k[3][Ly::CHUNKS], pro_v[Ly::CHUNKS];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) s.load_tile(s.krs, j, pro_k[j]);
+  s.load_tile(s.vrs, 0, pro_v);
+
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int row = s.qw0 + qb * 32 + s.li;
@@ -492,13 +499,9 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
 
   // ---- prologue: K_0, K_1, K_2 and V_0 into LDS, V slot 2 (standing for V_{-1}) and
   // P_{-1} zero; S_0; stage K_3 and V_1; operands of step 0's first chunk
-#pragma unroll 1
-  for (int j = 0; j < 3; ++j) {
-    s.load_tile(s.krs, j, s.stg_k);
-    s.store_tile(s.kslot + j * Ly::KSLOT, s.kst_off, Ly::KS, s.stg_k);
-  }
-  s.load_tile(s.vrs, 0, s.stg_v);
-  s.store_tile(s.vslot, s.vst_off, Ly::VS, s.stg_v);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) s.store_tile(s.kslot + j * Ly::KSLOT, s.kst_off, Ly::KS, pro_k[j]);
+  s.store_tile(s.vslot, s.vst_off, Ly::VS, pro_v);
 #pragma unroll
   for (int i = 0; i < Ly::CHUNKS; ++i) s.stg_v[i] = make_uint4(0, 0, 0, 0);
   s.store_tile(s.vslot + 2 * Ly::VSLOT, s.vst_off, Ly::VS, s.stg_v);

@@ -200,16 +200,19 @@ struct Attn {
     for (int r = 1; r < 16; ++r) a = fmaxf(a, sbuf[B][qb][r]);
     mx[qb] = a;
   }
+  // GUARD: a row may have seen no key yet (m = -inf).  Unmasked steady steps come
+  // after tile 0, which every row of the workgroup sees, so there m is finite and
+  // the infinite cases need no test.
+  template <bool GUARD>
   __device__ __forceinline__ void new_shift(int qb) {
     const float mt = c * max_pair(mx[qb]);  // -inf when no key of the tile is visible
     const float m_new = mt > m[qb] + kRescaleSlack ? mt : m[qb];
     // 0 when m was -inf, exactly 1 when unchanged (also for rows with no visible key yet)
-    alpha[qb] = m_new == -kInf ? 1.f : exp2_fast(m[qb] - m_new);
+    alpha[qb] = GUARD && m_new == -kInf ? 1.f : exp2_fast(m[qb] - m_new);
     m[qb] = m_new;
     l[qb] *= alpha[qb];
     lh[qb] *= alpha[qb];
-    msub[qb] = m_new == -kInf ? 0.f : m_new;
-    rs[qb] = 0.f;
+    msub[qb] = GUARD && m_new == -kInf ? 0.f : m_new;
   }
   // exponentials of scores e0 .. e0 + n - 1 (n a power of two dividing 16, so one
   // query block), added to the row sum as a pairwise tree (short dependency chains)
@@ -226,7 +229,7 @@ struct Attn {
     for (int w = n / 2; w >= 1; w /= 2)
 #pragma unroll
       for (int i = 0; i < w; ++i) t[i] += t[i + w];
-    rs[qb] += t[0];
+    rs[qb] = e0 % 16 == 0 ? t[0] : rs[qb] + t[0];  // the first run starts the tile's sum
   }
   __device__ __forceinline__ void pack(int B, int qb) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -267,12 +270,12 @@ struct Attn {
       for (int qb = 0; qb < kQB; ++qb) row_max(B, qb);
       if (NCH != 8) {
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) new_shift(qb);
+        for (int qb = 0; qb < kQB; ++qb) new_shift<GUARD>(qb);
       }
     }
     if (NCH == 8 && ch == 1) {
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) new_shift(qb);
+      for (int qb = 0; qb < kQB; ++qb) new_shift<GUARD>(qb);
     }
     static_assert(per * (last_exp - first_exp) == E && 16 % per == 0, "whole power-of-two runs of one query block");
     if (ch >= first_exp && ch < last_exp) exps<per>(B, (ch - first_exp) * per);

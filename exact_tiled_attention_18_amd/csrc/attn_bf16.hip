@@ -549,6 +549,18 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
   s.template step<true, 0>(0, sk_next, sk_w, sv_pv, sv_next, sv_w);
   advance();
   int t = 1;
+  // six steps per iteration (both buffer parities times the three slot phases), so
+  // every slot is a constant and LDS addresses fold into instruction offsets; the
+  // slot of tile j is j % 3, and the iteration starts at t = 1 mod 6
+  for (; t + 5 < steady_end; t += 6) {
+    s.template step<false, 1>(t, 2, 1, 0, 1, 2);
+    s.template step<false, 0>(t + 1, 0, 2, 1, 2, 0);
+    s.template step<false, 1>(t + 2, 1, 0, 2, 0, 1);
+    s.template step<false, 0>(t + 3, 2, 1, 0, 1, 2);
+    s.template step<false, 1>(t + 4, 0, 2, 1, 2, 0);
+    s.template step<false, 0>(t + 5, 1, 0, 2, 0, 1);
+  }
+  sk_next = (t + 1) % 3, sk_w = t % 3, sv_pv = (t + 2) % 3, sv_next = t % 3, sv_w = (t + 1) % 3;
   for (; t + 1 < steady_end; t += 2) {
     s.template step<false, 1>(t, sk_next, sk_w, sv_pv, sv_next, sv_w);
     advance();

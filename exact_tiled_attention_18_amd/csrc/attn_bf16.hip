@@ -316,17 +316,19 @@ struct Attn {
         kop[0] = read_k(sk_next == kSlots - 1 ? 0 : sk_next + 1, 0);
         vop[0] = read_v(sv_next, 0);
       }
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) snext[qb] = mfma(kop[ch & 1], qf[qb][ch], snext[qb]);
+      // P V first: its operands (V^T) are the chunk's newest LDS reads, so the one
+      // wait before it also covers the older K read of the score MFMA after it
       {
         const int db = ch % DB, mm = ch / DB;
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) oacc[db][qb] = mfma(vop[ch & 1], pold[qb][mm], oacc[db][qb]);
       }
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) snext[qb] = mfma(kop[ch & 1], qf[qb][ch], snext[qb]);
       softmax_slice<GUARD>(ch, B, t);
-      if (ch == 1) {
-        store_tile(kslot + sk_w * Ly::KSLOT, kst_off, Ly::KS, stg_k);
+      if (ch == 1) {  // V's piece was loaded last: waiting for it covers K's too
         store_tile(vslot + sv_w * Ly::VSLOT, vst_off, Ly::VS, stg_v);
+        store_tile(kslot + sk_w * Ly::KSLOT, kst_off, Ly::KS, stg_k);
       }
       if (ch == 2) {
         load_tile(krs, t + 4, stg_k);

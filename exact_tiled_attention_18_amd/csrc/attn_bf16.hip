@@ -194,10 +194,17 @@ struct Attn {
         if ((r & 7) + (r & 8) * 2 > lim) sbuf[B][qb][r] = -kInf;
     }
   }
+  // maxima as v_med3_f32 against +inf (the median of a, b and +inf is max(a, b)): the
+  // scores come straight from MFMAs and the partner's value from a lane swap, and
+  // fmaxf on such values costs an extra canonicalising instruction per operand
+  // (+inf comes from a register the compiler cannot see through: against the
+  // literal it folds the median back into a canonicalising maximum)
+  float pinf;
+  __device__ __forceinline__ float max2(float a, float b) const { return __builtin_amdgcn_fmed3f(a, b, pinf); }
   __device__ __forceinline__ void row_max(int B, int qb) {
-    float a = sbuf[B][qb][0];
+    float a = max2(sbuf[B][qb][0], sbuf[B][qb][1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) a = fmaxf(a, sbuf[B][qb][r]);
+    for (int r = 2; r < 16; ++r) a = fmaxf(a, sbuf[B][qb][r]);
     mx[qb] = a;
   }
   // GUARD: a row may have seen no key yet (m = -inf).  Unmasked steady steps come
@@ -205,7 +212,8 @@ struct Attn {
   // the infinite cases need no test.
   template <bool GUARD>
   __device__ __forceinline__ void new_shift(int qb) {
-    const float mt = c * max_pair(mx[qb]);  // -inf when no key of the tile is visible
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx[qb]), __float_as_uint(mx[qb]), false, false);
+    const float mt = c * max2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // -inf when no key is visible
     const float m_new = mt > m[qb] + kRescaleSlack ? mt : m[qb];
     // 0 when m was -inf, exactly 1 when unchanged (also for rows with no visible key yet)
     alpha[qb] = GUARD && m_new == -kInf ? 1.f : exp2_fast(m[qb] - m_new);
@@ -452,6 +460,8 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
   const int q0 = qblk * kBr;
   s.qw0 = q0 + (tid >> 6) * kW;
   s.c = c;
+  s.pinf = kInf;
+  asm volatile("" : "+v"(s.pinf));
   const int kv_end = CAUSAL ? min(gm.kn, gm.qpos + q0 + kBr) : gm.kn;
   const int nT = kv_end > 0 ? (kv_end + kBc - 1) / kBc : 0;
   // tiles 0 .. nFull-1 hold only keys that every query of the workgroup sees

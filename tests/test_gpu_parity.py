@@ -54,6 +54,50 @@ def test_scale_edge_cases(fa, dtype, scale):
         assert eo <= G.TOL[dtype][0] and el <= G.TOL[dtype][1]
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("where", ["k", "v"])
+def test_nan_input_propagates(fa, where, causal, d):
+    """A NaN in one element of key row j (of K or of V, head 1) reaches exactly the
+    query rows that see key j: their whole O row and LSE (K) or their O column (V)
+    are NaN. Every other output is finite and matches the oracle on the same inputs
+    with that element set to zero (a key a row does not see cannot change it)."""
+    B, H, N, j, c = 1, 2, 200, 77, 3
+    G.log(f"case nan in {where} causal={causal} d={d}")
+    q, k, v = synthetic.draw_qkv(B, H, N, d, seed=500 + d, dtype="bf16")
+    clean = {"k": k, "v": v}
+    bad = clean[where].clone()
+    bad[0, 1, j, c] = float("nan")
+    clean[where] = clean[where].clone()
+    clean[where][0, 1, j, c] = 0.0
+    args = {"k": k, "v": v}
+    args[where] = bad
+    o, lse = _run(fa, q, args["k"], args["v"], causal, d ** -0.5)
+    og, lg = G.to_np(o), G.to_np(lse)
+    sees = np.arange(N) >= j if causal else np.ones(N, dtype=bool)
+    if where == "k":
+        assert np.all(np.isnan(og[0, 1, sees])) and np.all(np.isnan(lg[0, 1, sees]))
+        finite_rows = np.nonzero(~sees)[0]
+    else:
+        assert np.all(np.isnan(og[0, 1, sees, c]))
+        assert np.all(np.isfinite(np.delete(og[0, 1, sees], c, axis=1))) and np.all(np.isfinite(lg[0, 1, sees]))
+        finite_rows = np.arange(N)
+    # head 0 entirely, and head 1 outside the NaN's reach, against the oracle
+    eo, el = G.compare_attention(o[:, :1], lse[:, :1], q[:, :1], clean["k"][:, :1], clean["v"][:, :1], causal,
+                                 d ** -0.5, "bf16")
+    assert eo <= G.TOL["bf16"][0] and el <= G.TOL["bf16"][1]
+    if len(finite_rows):
+        if where == "v":  # compare head 1 without column c
+            keep = [x for x in range(d) if x != c]
+            eo1, el1 = G.compare_attention(o[:, 1:, :, keep], lse[:, 1:], q[:, 1:], clean["k"][:, 1:],
+                                           clean["v"][:, 1:, :, keep], causal, d ** -0.5, "bf16", rows=finite_rows)
+        else:
+            eo1, el1 = G.compare_attention(o[:, 1:], lse[:, 1:], q[:, 1:], clean["k"][:, 1:], clean["v"][:, 1:],
+                                           causal, d ** -0.5, "bf16", rows=finite_rows)
+        G.log(f"  finite part: max|dO| {max(eo, eo1):.3e}  max|dLSE| {max(el, el1):.3e}")
+        assert eo1 <= G.TOL["bf16"][0] and el1 <= G.TOL["bf16"][1]
+
+
 def test_empty_problem_launches_nothing(fa):
     q = torch.empty((2, 3, 0, 64), dtype=torch.bfloat16, device=DEV)
     o, lse = fa.fa_fwd(q, q, q)

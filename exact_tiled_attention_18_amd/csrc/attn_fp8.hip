@@ -168,6 +168,10 @@ struct Attn8 {
       for (int r = 0; r < 16; ++r)
         if (kb * 32 + (r & 7) + (r & 8) * 2 > lim) sbuf[B][kb][r] = -kInf;
   }
+  // +inf from a register the compiler cannot see through: against the literal it folds
+  // the median back into a canonicalising maximum
+  float pinf;
+  __device__ __forceinline__ float max2(float a, float b) const { return __builtin_amdgcn_fmed3f(a, b, pinf); }
   __device__ __forceinline__ void softmax_slice(int ch, int B, int t, bool guard) {
     if (ch == 0) {
       // this tile's factors: multiplier, r = sv / svmax = 2^(e+1) f, 1 / f, E8M0 scale
@@ -180,18 +184,18 @@ struct Attn8 {
       if (guard) mask_scores(B, t);
       const f32x16& s0 = sbuf[B][0];
       const f32x16& s1 = sbuf[B][1];
-      // row maximum over the 32 scores: a tree of three-input maxima
-      float a[11];
+      // row maximum over the 32 scores: two chains of three-input maxima, each started
+      // by a median against +inf (max of its two operands; fmaxf on MFMA results
+      // would first canonicalise each operand), joined the same way across the lanes
+      float ma = max2(s0[0], s0[1]), mb = max2(s1[0], s1[1]);
 #pragma unroll
-      for (int i = 0; i < 5; ++i) a[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
-      a[5] = fmaxf(fmaxf(s0[15], s1[0]), s1[1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[6 + i] = fmaxf(fmaxf(s1[2 + 3 * i], s1[3 + 3 * i]), s1[4 + 3 * i]);
-      a[10] = fmaxf(s1[14], s1[15]);
-      const float b0 = fmaxf(fmaxf(a[0], a[1]), a[2]), b1 = fmaxf(fmaxf(a[3], a[4]), a[5]);
-      const float b2 = fmaxf(fmaxf(a[6], a[7]), a[8]), b3 = fmaxf(a[9], a[10]);
-      const float mx = fmaxf(fmaxf(b0, b1), fmaxf(b2, b3));
-      const float mt = cst * max_pair(mx);  // -inf when no key of the tile is visible
+      for (int r = 2; r < 16; ++r) {
+        ma = fmaxf(ma, s0[r]);
+        mb = fmaxf(mb, s1[r]);
+      }
+      const float mx = fmaxf(ma, mb);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      const float mt = cst * max2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // -inf when no key is visible
       const float m_new = mt > m + kSlack ? mt : m;
       alpha = m_new == -kInf ? 1.f : exp2_fast(m - m_new);
       m = m_new;
@@ -236,6 +240,9 @@ struct Attn8 {
         kop[0] = read_k(sk_next == kSlots - 1 ? 0 : sk_next + 1, 0);
         vop[0] = read_v(sv_next, 0);
       }
+      // P V first: V's operand is the chunk's newest LDS read, so the one wait before
+      // it also covers the K read of the score MFMA after it
+      oacc[ch] = mfma_fp8_bs(vop[ch & 1], pold, oacc[ch], psold);
       {
         const int kb = ch & 1, kk = ch >> 1;
         if (kk == 0) {
@@ -245,11 +252,10 @@ struct Attn8 {
           snext[kb] = mfma_fp8(kop[ch & 1], qf[1], snext[kb]);
         }
       }
-      oacc[ch] = mfma_fp8_bs(vop[ch & 1], pold, oacc[ch], psold);
       softmax_slice(ch, B, t, GUARD);
-      if (ch == 1) {
-        store_k(sk_w, stg_k);
+      if (ch == 1) {  // V's piece was loaded last: waiting for it covers K's too
         store_v(sv_w, stg_v);
+        store_k(sk_w, stg_k);
       }
       if (ch == 2) {
         load_scales(t + 1);
@@ -309,6 +315,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   s.ksrs = __builtin_amdgcn_make_buffer_rsrc((void*)s.ks_head, (short)0, nTiles * 4, kRsrcWord3);
   s.vsrs = __builtin_amdgcn_make_buffer_rsrc((void*)s.vs_head, (short)0, nTiles * 4, kRsrcWord3);
   s.N = N;
+  s.pinf = kInf;
+  asm volatile("" : "+v"(s.pinf));
   s.nTiles = nTiles;
   s.ldv = ldv;
   const int tid = threadIdx.x;

@@ -825,6 +825,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
     w.load(t0 + 2);
     w.read_grad(0, 0, 3);
     int t = t0;
+    // four steps per iteration (two parities times the four buffers): buffer indices
+    // are constants, so LDS addresses fold into instruction offsets
+    for (; t + 3 < nQT; t += 4) {
+      w.template step<0>(t, 0, t + 3 < nQT);
+      w.template step<1>(t + 1, 1, t + 4 < nQT);
+      w.template step<0>(t + 2, 2, t + 5 < nQT);
+      w.template step<1>(t + 3, 3, t + 6 < nQT);
+    }
     for (; t + 1 < nQT; t += 2) {
       w.template step<0>(t, (t - t0) % NB, t + 3 < nQT);
       w.template step<1>(t + 1, (t + 1 - t0) % NB, t + 4 < nQT);

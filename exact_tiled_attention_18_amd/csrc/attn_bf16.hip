@@ -427,12 +427,22 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
     o = static_cast<float*>(o) + (size_t)sp * BH * gm.nq * D;
     lse += (size_t)sp * BH * gm.nq;
   }
-  // work item -> (query block, head): heaviest causal blocks first; consecutive
-  // ids go to different XCDs, so with B*H a multiple of 8 all blocks of a head
-  // share one XCD's L2
+  // work item -> (query block, head).  Workgroup ids go to the 8 XCDs in turn, so
+  // with B*H a multiple of 8 every block of a head runs on one XCD.  Causal: the
+  // heaviest blocks first, heads interleaved.  Otherwise the blocks of a head are
+  // consecutive within their XCD, so they run together and read the head's K/V
+  // through that XCD's L2 (interleaved heads would spread each XCD's concurrent
+  // workgroups over more heads' K/V than its L2 holds).
   const int L = blockIdx.x;
-  const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
-  const int bh = L % BH;
+  int qblk, bh;
+  if (CAUSAL || PART || BH % 8 != 0) {
+    qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
+    bh = L % BH;
+  } else {
+    const int slot = L / 8;
+    qblk = slot % nQB;
+    bh = (slot / nQB) * 8 + L % 8;
+  }
   const int N = gm.nq;  // query rows
   const size_t base = (size_t)bh * N * D;
   const size_t kbase = ((size_t)bh * gm.nk + gm.k0) * D;

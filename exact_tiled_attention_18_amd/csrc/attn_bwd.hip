@@ -42,6 +42,16 @@ namespace {
 
 constexpr int kT = 32;  // rows per streamed tile (keys in dQ, queries in dK/dV)
 
+// Work item L -> (block, head) when every block of a launch costs the same (non-causal,
+// B*H a multiple of 8): workgroup ids go to the 8 XCDs in turn, and within an XCD the
+// blocks of a head are consecutive, so they run together and share the head's data in
+// that XCD's L2.
+__device__ __forceinline__ void grouped_item(int L, int BH, int nblk, int& blk, int& bh) {
+  const int slot = L / 8;
+  blk = slot % nblk;
+  bh = (slot / nblk) * 8 + L % 8;
+}
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -151,8 +161,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const uint16_t* __restrict_
   auto vbuf = [&](int b) { return smem + (2 + b) * T::BYTES; };
 
   const int L = blockIdx.x;
-  const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
-  const int bh = L % BH;
+  int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
+  int bh = L % BH;
+  if (!CAUSAL && BH % 8 == 0) grouped_item(L, BH, nQB, qblk, bh);
   const size_t base = (size_t)bh * N * D;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int q0 = qblk * kBr;
@@ -364,8 +375,9 @@ __global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __rest
 
   W w;
   const int L = blockIdx.x;
-  const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
-  const int bh = L % BH;
+  int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
+  int bh = L % BH;
+  if (!CAUSAL && BH % 8 == 0) grouped_item(L, BH, nQB, qblk, bh);
   const size_t base = (size_t)bh * N * D;
   const int tid = threadIdx.x, lane = tid & 63;
   w.g = lane >> 5;
@@ -462,8 +474,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   auto dbuf = [&](int b) { return smem + (2 + b) * T::BYTES; };
 
   const int L = blockIdx.x;
-  const int kblk = L / BH;  // smallest key blocks (most causal work) first
-  const int bh = L % BH;
+  int kblk = L / BH;  // smallest key blocks (most causal work) first
+  int bh = L % BH;
+  if (!CAUSAL && BH % 8 == 0) grouped_item(L, BH, (int)(gridDim.x / BH), kblk, bh);
   const size_t base = (size_t)bh * N * D;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, li = lane & 31;
   const int k0 = kblk * kBk;
@@ -753,8 +766,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
 
   W w;
   const int L = blockIdx.x;
-  const int kblk = L / BH;  // smallest key blocks (most causal work) first
-  const int bh = L % BH;
+  int kblk = L / BH;  // smallest key blocks (most causal work) first
+  int bh = L % BH;
+  if (!CAUSAL && BH % 8 == 0) grouped_item(L, BH, (int)(gridDim.x / BH), kblk, bh);
   const size_t base = (size_t)bh * N * D;
   w.tid = threadIdx.x;
   const int lane = w.tid & 63;

@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -202,6 +203,30 @@ def warm_up(fn, steps: int, min_s: float) -> tuple[int, float]:
     return n, time.perf_counter() - t0
 
 
+def extra_windows(fn, iters: int, n: int) -> list[float]:
+    """Seconds per call of fn in n further windows of iters back-to-back calls (after
+    the timed region; the reported value stays the timed region's)."""
+    return [time_loop(fn, iters) for _ in range(n)]
+
+
+def cold_cache_time(fn, iters: int, dev) -> float:
+    """Median seconds of single calls of fn, each after a 512 MiB write that evicts the
+    L2s and the 256 MB MALL, timed with HIP events around the call alone."""
+    junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream()
+    times = []
+    for i in range(iters):
+        junk.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    del junk
+    return statistics.median(times)
+
+
 def cpu_baseline(w, budget_s: float):
     """The fp64 oracle, timed on this host on a bounded sample of the workload's heads."""
     from oracle import attention as A
@@ -340,6 +365,10 @@ def main():
                     choices=[w.name for w in synthetic.WORKLOADS])
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--windows", type=int, default=5,
+                    help="after the timed region, this many more windows of --steps steps (median and best reported)")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="also time single steps after a 512 MiB write that evicts L2 and MALL (forward workloads)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (fa_bwd) of a bf16 workload instead of the forward")
     ap.add_argument("--split-kv", action="store_true",
@@ -388,6 +417,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     tflops = w.flops() / sec / 1e12
+    wins = sorted(extra_windows(step, args.steps, args.windows)) if args.windows > 0 else []
+    cold = cold_cache_time(step, min(args.steps, 50), dev) if args.cold_cache else None
 
     # dominant kernel: the attention launch (for fp8, timed apart from the pre-pass)
     if parts is None:
@@ -418,6 +449,14 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "scale": "1/sqrt(d)", "flops_per_step": w.flops()},
         "frac_of_peak": round(tflops / peak, 4), "wall_s_timed": round(wall, 4),
+        "windows": None if not wins else {
+            "count": len(wins), "steps_each": args.steps,
+            "ms_per_step_median": round(statistics.median(wins) * 1e3, 5), "ms_per_step_best": round(wins[0] * 1e3, 5),
+            "value_median": round(w.flops() / statistics.median(wins) / 1e12, 2),
+            "value_best": round(w.flops() / wins[0] / 1e12, 2)},
+        "cold_cache": None if cold is None else {
+            "ms_per_step_median": round(cold * 1e3, 5), "value": round(w.flops() / cold / 1e12, 2),
+            "note": "single launches, each after a 512 MiB write that evicts L2 and MALL"},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -443,6 +443,14 @@ __global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __rest
     w.load(2);
     w.read_kt(0, 0, 3);
     int t = 0;
+    // four steps per iteration (two parities times the four buffers): buffer indices
+    // are constants, so LDS addresses fold into instruction offsets
+    for (; t + 3 < nT; t += 4) {
+      w.template step<0>(t, 0, t + 3 < nT, qlim);
+      w.template step<1>(t + 1, 1, t + 4 < nT, qlim);
+      w.template step<0>(t + 2, 2, t + 5 < nT, qlim);
+      w.template step<1>(t + 3, 3, t + 6 < nT, qlim);
+    }
     for (; t + 1 < nT; t += 2) {
       w.template step<0>(t, t % NB, t + 3 < nT, qlim);
       w.template step<1>(t + 1, (t + 1) % NB, t + 4 < nT, qlim);

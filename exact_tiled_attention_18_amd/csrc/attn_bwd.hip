@@ -675,8 +675,9 @@ struct DkDv {
       dl[r] = bv[r];
     }
   }
-  // P and dS of score elements [e0, e0 + EPC) of tile t (parity B)
-  template <int B>
+  // P and dS of score elements [e0, e0 + EPC) of tile t (parity B); without G every
+  // query of the tile is below N and sees every key of the block
+  template <int B, bool G>
   __device__ __forceinline__ void grad_slice(int t, int e0) {
 #pragma unroll
     for (int e = e0; e < e0 + EPC; e += 2) {
@@ -685,7 +686,7 @@ struct DkDv {
       for (int h = 0; h < 2; ++h) {
         const int r = e + h;
         const int qr = t * kT + row_of_reg(r, g);
-        const bool vis = qr < N && kj < N && (!CAUSAL || kj <= qr);
+        const bool vis = !G || (qr < N && kj < N && (!CAUSAL || kj <= qr));
         p2[h] = vis ? exp2_fast(fmaf(s[B][r], c, -ls[r])) : 0.f;
         d2[h] = p2[h] * (dp[B][r] - dl[r]);
       }
@@ -709,7 +710,7 @@ struct DkDv {
   // one step for tile t in buffer cur (parity B = (t - t0) & 1); the dV/dK operands
   // of its chunk 0 were read by the previous step (tile t+1's were written before
   // the last barrier only, so its S/dP operands are read here)
-  template <int B>
+  template <int B, bool G = true>
   __device__ __forceinline__ void step(int t, int cur, bool more) {
     const int bn = (cur + 1) % NB, bo = (cur + NB - 1) % NB, bw = (cur + 2) % NB;
     read_sdp(0, 0, bn);
@@ -729,7 +730,7 @@ struct DkDv {
       s[B ^ 1] = mfma(opq[sl], kf[ch], s[B ^ 1]);
       dka[db] = mfma(opk[sl], word8(sw[B ^ 1], mm), dka[db]);
       dp[B ^ 1] = mfma(opd[sl], vf[ch], dp[B ^ 1]);
-      grad_slice<B>(t, ch * EPC);
+      grad_slice<B, G>(t, ch * EPC);
       if (ch == 1) store(bw);
       if (ch == 2 && more) load(t + 3);
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
@@ -848,13 +849,23 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
     w.read_grad(0, 0, 3);
     int t = t0;
     // four steps per iteration (two parities times the four buffers): buffer indices
-    // are constants, so LDS addresses fold into instruction offsets
-    for (; t + 3 < nQT; t += 4) {
-      w.template step<0>(t, 0, t + 3 < nQT);
-      w.template step<1>(t + 1, 1, t + 4 < nQT);
-      w.template step<0>(t + 2, 2, t + 5 < nQT);
-      w.template step<1>(t + 3, 3, t + 6 < nQT);
+    // are constants, so LDS addresses fold into instruction offsets.  Query tiles
+    // [t0 + 4, tf) (causal; [0, tf) otherwise) lie wholly below N and after every key of
+    // a block that ends at or before N: they skip the per-element visibility test.
+    const int tf = k0 + kBk <= N ? N / kT : 0;
+    auto quad = [&](auto guard) {
+      constexpr bool G = decltype(guard)::value;
+      w.template step<0, G>(t, 0, t + 3 < nQT);
+      w.template step<1, G>(t + 1, 1, t + 4 < nQT);
+      w.template step<0, G>(t + 2, 2, t + 5 < nQT);
+      w.template step<1, G>(t + 3, 3, t + 6 < nQT);
+    };
+    if (CAUSAL && t + 3 < nQT) {
+      quad(std::true_type{});
+      t += 4;
     }
+    for (; t + 3 < tf; t += 4) quad(std::false_type{});
+    for (; t + 3 < nQT; t += 4) quad(std::true_type{});
     for (; t + 1 < nQT; t += 2) {
       w.template step<0>(t, (t - t0) % NB, t + 3 < nQT);
       w.template step<1>(t + 1, (t + 1 - t0) % NB, t + 4 < nQT);

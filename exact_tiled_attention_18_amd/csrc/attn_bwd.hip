@@ -33,7 +33,9 @@
 // A negative scale flips every sign bit of Q, a zero scale zeroes Q (the
 // kernels then use the positive multiplier |scale| * log2(e)): dQ = scale *
 // (dS K) and dK = |scale| * (dS^T Q') for the flipped Q', which are the
-// gradients of the original problem.
+// gradients of the original problem.  The pipelined dK/dV kernel instead takes Q
+// unchanged with the signed multiplier scale * log2(e) and dK = scale * (dS^T Q),
+// the same products with the sign moved out of the operand.
 #include "fa_device.h"
 #include "launch.h"
 
@@ -605,9 +607,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------- dK, dV (d = 128)
-// Software pipeline over query tiles: step t issues the MFMAs of S_{t+1} = Q'_{t+1} K^T
+// Software pipeline over query tiles: step t issues the MFMAs of S_{t+1} = Q_{t+1} K^T
 // and dP_{t+1} = dO_{t+1} V^T, the MFMAs of dV += dO_{t-1}^T P_{t-1} and
-// dK += Q'_{t-1}^T dS_{t-1}, and the vector work that turns S_t, dP_t into P_t, dS_t;
+// dK += Q_{t-1}^T dS_{t-1}, and the vector work that turns S_t, dP_t into P_t, dS_t;
 // none depends on another, so they are interleaved chunk by chunk.  Four LDS
 // buffers hold tiles t-1 .. t+2 (tile t waits there for its dV/dK products in the
 // next step); tile t+2 is written from registers loaded one step earlier.
@@ -635,8 +637,7 @@ struct DkDv {
   const float* delta_h;
   int N, tid, g, li, kj, qrow, tr_off;
   int ld_off[kPer], st_off[kPer];
-  float c;
-  uint32_t qxor, qand;
+  float c;  // scale * log2(e), signed: Q enters unchanged
 
   __device__ __forceinline__ char* qbuf(int b) const { return smem + b * T::BYTES; }
   __device__ __forceinline__ char* dbuf(int b) const { return smem + (NB + b) * T::BYTES; }
@@ -644,8 +645,7 @@ struct DkDv {
   __device__ __forceinline__ void load(int t) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ld_off[i] + t * kT * D * 2, 0, 0));
-      sq[i] = make_uint4((a.x ^ qxor) & qand, (a.y ^ qxor) & qand, (a.z ^ qxor) & qand, (a.w ^ qxor) & qand);
+      sq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ld_off[i] + t * kT * D * 2, 0, 0));
       sd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, ld_off[i] + t * kT * D * 2, 0, 0));
     }
     if (tid < 2 * kT) {
@@ -765,8 +765,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int BH, int N, float c, float dk_mul, uint32_t qxor,
-    uint32_t qand) {
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int BH, int N, float c, float dk_mul) {
   using W = DkDv<D, CAUSAL>;
   using T = Tile<D>;
   constexpr int DK = W::DK, DB = W::DB, NB = W::NB, kPer = W::kPer, kBk = 128;
@@ -787,8 +786,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
   w.kj = k0 + (w.tid >> 6) * 32 + w.li;  // this lane's key
   w.N = N;
   w.c = c;
-  w.qxor = qxor;
-  w.qand = qand;
   w.smem = smem;
   w.stat = stat;
   w.lse_h = lse + (size_t)bh * N;
@@ -909,8 +906,8 @@ hipError_t launch_d(const BwdArgs& a) {
   // plain one, which fits two wavefronts per SIMD and hides its latencies with the second
   if constexpr (D == 128)
     hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(256), 0, a.stream, q, k,
-                       v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N, c,
-                       fabsf(a.scale), qxor, qand);
+                       v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N,
+                       a.scale * kLog2e, a.scale);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(256), 0, a.stream, q, k, v,
                        dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N, c,

@@ -9,7 +9,11 @@ Inputs are resident in HBM before the timed region.  FLOPs counted:
 4*B*H*N^2*d, halved when causal (masking waste and exps are not counted).
 
 Prints exactly one JSON line on stdout; per-kernel details go to stderr.
-The default workload is bf16 causal B=4 H=16 N=2048 d=128.
+The default workload is bf16 causal B=1 H=32 N=16384 d=128, the largest
+workload that runs on one GPU; the same line also carries, under "extra",
+bf16 causal B=4 H=16 N=2048 d=128 and the fp8 causal B=2 H=16 N=8192 d=128
+workload (pre-pass and attention kernel timed apart), each with its own
+roofline.
 """
 from __future__ import annotations
 
@@ -227,29 +231,102 @@ def cold_cache_time(fn, iters: int, dev) -> float:
     return statistics.median(times)
 
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle, timed on this host on a bounded sample of the workload's heads."""
-    from oracle import attention as A
-
+def host_info() -> dict:
+    """The host the oracle runs on: usable cores, BLAS library and threads, RAM."""
+    info = {"cores_affinity": len(os.sched_getaffinity(0)), "blas": None, "blas_threads": None, "ram_gib": None}
     try:
         import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+        blas = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = int(blas[0].get("num_threads", 1))
     except Exception:  # noqa: BLE001
-        threads = 1
+        pass
+    try:
+        info["ram_gib"] = round(os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES") / 2 ** 30, 1)
+    except (ValueError, OSError):
+        pass
+    return info
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle, timed on this host on a bounded sample of the workload's
+    heads: whole heads, cycled until budget_s has passed (at least one).  The
+    oracle materialises the full N x N score matrix, so it performs 4*N^2*d
+    FLOPs per head even when causal; `value` uses the same counted FLOPs as the
+    GPU line (halved for causal), `value_full_nxn` the FLOPs the oracle ran."""
+    from oracle import attention as A
+
+    hi = host_info()
     q, k, v, _ = synthetic.workload_inputs(w)
     heads = 0
     nbh = w.B * w.H
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:  # cycle over the heads until the budget is spent
+    while heads == 0 or time.perf_counter() - t0 < budget_s:  # cycle over the heads until the budget is spent
         b, h = divmod(heads % nbh, w.H)
         sl = (slice(b, b + 1), slice(h, h + 1))
         A.reference(q[sl], k[sl], v[sl], w.causal, w.scale)
         heads += 1
     dt = time.perf_counter() - t0
     flops = w.flops() * heads / nbh
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} head evaluations ({heads / nbh:.2f} passes over the {nbh} heads) of {w.name}, "
-                      f"full N x N fp64 oracle, {dt:.1f} s"}
+    full = 4.0 * w.N * w.N * w.d * heads
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": hi["blas_threads"] or 1,
+            "kind": "oracle",
+            "sample": f"{heads} whole-head evaluations ({heads / nbh:.3f} of the {nbh} heads) of {w.name}, "
+                      f"full N x N fp64 oracle, {dt:.1f} s",
+            "flop_basis": "counted FLOPs (4*B*H*N^2*d, halved when causal) of the heads evaluated; "
+                          "the oracle itself computes the full N x N product",
+            "value_full_nxn": round(full / dt / 1e12, 6),
+            "cores_affinity": hi["cores_affinity"], "blas": hi["blas"], "blas_threads": hi["blas_threads"],
+            "host_ram_gib": hi["ram_gib"], "seconds": round(dt, 2)}
+
+
+class SclkSampler:
+    """Samples the shader clock the driver reports (the starred level of
+    pp_dpm_sclk, MHz) from a background thread while the GPU works; None when
+    the file is not readable."""
+
+    def __init__(self, period_s: float = 0.02):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples: list[float] = []
+        self.period = period_s
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for p in self.paths:
+            try:
+                for line in open(p).read().splitlines():
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            x = self._read()
+            if x is not None:
+                self.samples.append(x)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._t.is_alive():
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"mhz_median": statistics.median(self.samples), "mhz_min": min(self.samples),
+                "mhz_max": max(self.samples), "samples": len(self.samples), "source": "pp_dpm_sclk (starred level)"}
 
 
 def bench_backward(fa, w, dev, args):
@@ -284,6 +361,9 @@ def bench_backward(fa, w, dev, args):
            "cpu_baseline": None}
     print(json.dumps(rec), flush=True)
 
+
+DEFAULT_WORKLOAD = "bf16_causal_b1h32n16384d128"
+EXTRA_WORKLOADS = ("bf16_causal_b4h16n2048d128", "fp8_causal_b2h16n8192d128_outliers")
 
 DECODE = {"B": 4, "H": 16, "Nq": 16, "Nk": 16384, "d": 128, "n_splits": 8, "seed": 1200}
 
@@ -361,8 +441,12 @@ def main():
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this many seconds of back-to-back steps have run "
                          "(the clock ramps up under sustained load); 'warmup' in the output is the count run")
-    ap.add_argument("--workload", default="bf16_causal_b4h16n2048d128",
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=[w.name for w in synthetic.WORKLOADS])
+    ap.add_argument("--no-extras", dest="extras", action="store_false",
+                    help="with the default workload, do not add the N = 2048 and fp8 workloads under 'extra'")
+    ap.add_argument("--extra-warmup-s", type=float, default=0.3,
+                    help="minimum warm-up seconds of each extra workload")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--windows", type=int, default=5,
@@ -409,57 +493,95 @@ def main():
         return
     if args.backward:
         return bench_backward(fa, w, dev, args)
-    step, parts = make_step(fa, w, dev)
-    wn, ws = warm_up(step, args.warmup, args.min_warmup_s)
+    with SclkSampler() as sclk:
+        main_m = measure_forward(fa, w, dev, args.steps, args.warmup, args.min_warmup_s, args.windows,
+                                 args.cold_cache)
+        extra = {}
+        if args.extras and w.name == DEFAULT_WORKLOAD:
+            for name in EXTRA_WORKLOADS:
+                ew = synthetic.workload(name)
+                m = measure_forward(fa, ew, dev, args.steps, args.warmup, args.extra_warmup_s, 0, False)
+                extra[name] = forward_record(ew, m)
+    r = forward_record(w, main_m)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
+    rec = {
+        "metric": "attention fwd TFLOP/s at 1 MI355X and % of dense MFMA peak (bf16, fp8)",
+        "value": r["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": main_m["warmup"], "warmup_requested": args.warmup, "warmup_s": main_m["warmup_s"],
+        "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": r["config"], "frac_of_peak": r["frac_of_peak"], "wall_s_timed": main_m["wall_s"],
+        "windows": r["windows"], "cold_cache": r["cold_cache"],
+        "roofline": r["roofline"], "cpu_baseline": cpu,
+        "sclk": sclk.summary(),
+        "extra": extra or None,
+    }
+    print(json.dumps(rec), flush=True)
 
+
+def measure_forward(fa, w, dev, steps: int, warmup: int, min_warmup_s: float, windows: int, cold: bool) -> dict:
+    """Times `steps` back-to-back steps of a forward workload after the warm-up,
+    then the attention kernel alone (and, for fp8, the pre-pass alone)."""
+    step, parts = make_step(fa, w, dev)
+    wn, ws = warm_up(step, warmup, min_warmup_s)
     t0 = time.perf_counter()
-    sec = time_loop(step, args.steps)
+    sec = time_loop(step, steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    tflops = w.flops() / sec / 1e12
-    wins = sorted(extra_windows(step, args.steps, args.windows)) if args.windows > 0 else []
-    cold = cold_cache_time(step, min(args.steps, 50), dev) if args.cold_cache else None
-
-    # dominant kernel: the attention launch (for fp8, timed apart from the pre-pass)
+    wins = sorted(extra_windows(step, steps, windows)) if windows > 0 else []
+    cold_s = cold_cache_time(step, min(steps, 50), dev) if cold else None
+    pre_sec = None
     if parts is None:
         k_sec = sec
     else:
         prepass, attn = parts
-        pre_sec = time_loop(prepass, args.steps)
-        k_sec = time_loop(attn, args.steps)
-        pre_bytes = 3 * (2 + 1) * w.B * w.H * w.N * w.d + 3 * 4 * w.B * w.H * ((w.N + 127) // 128)
-        eprint(f"fp8 pre-pass: {pre_sec * 1e6:.1f} us for 3 tensors, {pre_bytes / pre_sec / 1e9:.0f} GB/s "
-               f"({pre_bytes / pre_sec / 1e9 / HBM_GBPS:.1%} of 8 TB/s)")
+        pre_sec = time_loop(prepass, steps)
+        k_sec = time_loop(attn, steps)
+    return {"sec": sec, "k_sec": k_sec, "pre_sec": pre_sec, "wins": wins, "cold": cold_s, "warmup": wn,
+            "warmup_s": round(ws, 3), "wall_s": round(wall, 4), "steps": steps}
+
+
+def forward_record(w, m: dict) -> dict:
+    """The figures of one forward workload: step throughput, the attention kernel's
+    roofline (and the fp8 pre-pass against HBM)."""
+    sec, k_sec = m["sec"], m["k_sec"]
+    tflops = w.flops() / sec / 1e12
     k_tflops = w.flops() / k_sec / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     eprint(f"{w.name}: step {sec * 1e6:.1f} us ({tflops:.1f} TFLOP/s); attention kernel {k_sec * 1e6:.1f} us "
            f"= {k_tflops:.1f} TFLOP/s = {k_tflops / peak:.1%} of {peak} TFLOP/s; algorithmic HBM "
            f"{algorithmic_bytes(w) / k_sec / 1e9:.0f} GB/s")
-
-    roofline = {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(k_tflops / peak, 4),
-                "traffic": hbm_traffic(w.name, KERNEL_SOURCE[w.dtype])}
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
-    rec = {
-        "metric": "attention fwd TFLOP/s at 1 MI355X and % of dense MFMA peak (bf16, fp8)",
-        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": wn, "warmup_requested": args.warmup, "warmup_s": round(ws, 3),
-        "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "scale": "1/sqrt(d)", "flops_per_step": w.flops()},
-        "frac_of_peak": round(tflops / peak, 4), "wall_s_timed": round(wall, 4),
-        "windows": None if not wins else {
-            "count": len(wins), "steps_each": args.steps,
+    rec = {"value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(sec * 1e3, 5), "steps": m["steps"],
+           "warmup": m["warmup"], "dtype": w.dtype,
+           "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                      "scale": "1/sqrt(d)", "flops_per_step": w.flops()},
+           "frac_of_peak": round(tflops / peak, 4),
+           "roofline": {"bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(k_tflops / peak, 4), "traffic": hbm_traffic(w.name, KERNEL_SOURCE[w.dtype]),
+                        "kernel_ms": round(k_sec * 1e3, 5),
+                        "algorithmic_bytes": algorithmic_bytes(w)},
+           "windows": None, "cold_cache": None}
+    wins = m["wins"]
+    if wins:
+        rec["windows"] = {
+            "count": len(wins), "steps_each": m["steps"],
             "ms_per_step_median": round(statistics.median(wins) * 1e3, 5), "ms_per_step_best": round(wins[0] * 1e3, 5),
             "value_median": round(w.flops() / statistics.median(wins) / 1e12, 2),
-            "value_best": round(w.flops() / wins[0] / 1e12, 2)},
-        "cold_cache": None if cold is None else {
-            "ms_per_step_median": round(cold * 1e3, 5), "value": round(w.flops() / cold / 1e12, 2),
-            "note": "single launches, each after a 512 MiB write that evicts L2 and MALL"},
-        "roofline": roofline, "cpu_baseline": cpu,
-    }
-    print(json.dumps(rec), flush=True)
+            "value_best": round(w.flops() / wins[0] / 1e12, 2)}
+    if m["cold"] is not None:
+        rec["cold_cache"] = {"ms_per_step_median": round(m["cold"] * 1e3, 5),
+                             "value": round(w.flops() / m["cold"] / 1e12, 2),
+                             "note": "single launches, each after a 512 MiB write that evicts L2 and MALL"}
+    if m["pre_sec"] is not None:
+        pre_sec = m["pre_sec"]
+        pre_bytes = 3 * (2 + 1) * w.B * w.H * w.N * w.d + 3 * 4 * w.B * w.H * ((w.N + 127) // 128)
+        eprint(f"fp8 pre-pass: {pre_sec * 1e6:.1f} us for 3 tensors, {pre_bytes / pre_sec / 1e9:.0f} GB/s "
+               f"({pre_bytes / pre_sec / 1e9 / HBM_GBPS:.1%} of 8 TB/s)")
+        rec["prepass"] = {"ms": round(pre_sec * 1e3, 5), "bytes": pre_bytes,
+                          "roofline": {"bound": "hbm", "achieved": round(pre_bytes / pre_sec / 1e9, 1),
+                                       "peak": HBM_GBPS, "unit": "GB/s",
+                                       "frac": round(pre_bytes / pre_sec / 1e9 / HBM_GBPS, 4)}}
+    return rec
 
 
 if __name__ == "__main__":

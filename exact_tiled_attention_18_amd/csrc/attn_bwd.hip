@@ -791,7 +791,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
   w.lse_h = lse + (size_t)bh * N;
   w.delta_h = delta + (size_t)bh * N;
   constexpr int kRsrcWord3 = 0x00020000;
-  w.qrs = __builtin_amdgcn_make_buffer_rsrc((void*)(q + base), (short)0, N * D * 2, kRsrcWord3);
+  // a zero scale reads Q as zeros (a buffer of no bytes): the scores are then exactly 0
+  // even where Q K^T would overflow, as in the forward, which zeroes Q
+  w.qrs = __builtin_amdgcn_make_buffer_rsrc((void*)(q + base), (short)0, c == 0.f ? 0 : N * D * 2, kRsrcWord3);
   w.drs = __builtin_amdgcn_make_buffer_rsrc((void*)(dout + base), (short)0, N * D * 2, kRsrcWord3);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {

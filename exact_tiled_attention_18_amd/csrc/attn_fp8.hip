@@ -38,11 +38,21 @@
 // operand of the P V instruction.  The accumulator is then in units of
 // v_scale_max / 2^6 for every tile (no per-tile rescaling), and the rounding
 // of P keeps the same relative precision whatever V's scales are.  The
-// running row sum adds the probabilities times 2^6, so O = acc *
-// v_scale_max / sum and LSE follows from the same sum.  The softmax shift
+// running row sums add the probabilities times 2^6, so O = acc *
+// v_scale_max / (rounded sum) and LSE follows from the fp32 sum.  The softmax shift
 // moves lazily, only when a row maximum exceeds it by more than 2 (log2
 // units): probabilities stay below 4, so the rounded values stay below 256,
 // inside the e4m3 range (448).
+//
+// Two row sums, as in the bf16 kernel.  l adds the fp32 probabilities and gives
+// LSE.  lh adds the e4m3-rounded probabilities that actually enter P V and
+// normalises O, which makes O an exact weighted mean of the dequantised V rows
+// under the weights used (with l, a row dominated by one key would carry that
+// key's rounding error, up to 2^-4 of |v|).  The rounded sum of a tile is taken
+// on the matrix core: four v_mfma_f32_16x16x32_fp8_fp8 against a constant
+// selector of ones, whose rows pick, for every lane, the two lane groups that
+// hold its own query (lanes l and l + 32), so that accumulator register 0 of
+// lane l ends up holding the sum of the tile's 64 codes of query l % 32.
 //
 // A negative scale flips the sign bit of every Q code (exact), a zero scale
 // zeroes Q; the kernel always works with a positive multiplier.
@@ -105,9 +115,11 @@ struct Attn8 {
   f32x16 sbuf[2][2];    // S^T of two consecutive tiles, two 32-key halves each
   i32x8 pbuf[2];        // P8^T of two consecutive tiles
   int pscale[2];        // their E8M0 block scales
+  float pinvf[2];       // and the 1 / f of their tiles (for the rounded row sum)
+  long sel;             // selector of ones for the rounded row sums (A operand, 8 codes)
   i32x8 kop[2], vop[2]; // operand prefetch, by chunk parity
   uint4 stg_k, stg_v;   // this thread's piece of the next K8 / V8^T tiles
-  float m, l, alpha, msub, rs;
+  float m, l, lh, alpha, msub, rs;
   float cst, inv_frac;  // softmax multiplier and 1 / f of the tile being softmaxed
   int psc;               // its E8M0 scale 127 + e + 1
   float ks_n, vs_n;      // raw K and V tile scales of the next tile (loaded one step ahead)
@@ -133,6 +145,19 @@ struct Attn8 {
   }
   __device__ __forceinline__ i32x8 read_v(int slot, int ch) const {
     return lds_read32(vslot + slot * kVSlot + vrd_off + ch * 32 * kVS);
+  }
+  // sum of the 64 rounded probabilities (codes) of this lane's query in P8^T p, in
+  // lane register 0 of a 16x16 accumulator: lane l holds keys of query l % 32, and
+  // lane group G = l / 16 of the A operand selects, for output row 4 G', the lane
+  // groups holding query 16 (G' % 2) + (l % 16), namely G' % 2 and G' % 2 + 2
+  __device__ __forceinline__ float rounded_sum(const i32x8& p) const {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long b = (long)(((unsigned long)(uint32_t)p[2 * i + 1] << 32) | (uint32_t)p[2 * i]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(sel, b, acc, 0, 0, 0);
+    }
+    return acc[0];
   }
   // this thread's 16-byte pieces of K8 tile t (row-major) and V8^T tile t (row d, 16 keys);
   // buffer loads return zeros past the end of the head's data
@@ -222,6 +247,7 @@ struct Attn8 {
           pbuf[B][kb * 4 + hh * 2 + 1] = (int)pack_fp8x4(s[b0 + 4], s[b0 + 5], s[b0 + 6], s[b0 + 7]);
         }
       pscale[B] = psc;
+      pinvf[B] = inv_frac;
       l += rs * inv_frac;
     }
   }
@@ -231,6 +257,7 @@ struct Attn8 {
     f32x16(&snext)[2] = sbuf[B ^ 1];
     const i32x8& pold = pbuf[B ^ 1];
     const int psold = pscale[B ^ 1];
+    float rsum = 0.f;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       if (ch + 1 < NCH) {
@@ -243,6 +270,7 @@ struct Attn8 {
       // P V first: V's operand is the chunk's newest LDS read, so the one wait before
       // it also covers the K read of the score MFMA after it
       oacc[ch] = mfma_fp8_bs(vop[ch & 1], pold, oacc[ch], psold);
+      if (ch == 0) rsum = rounded_sum(pold);
       {
         const int kb = ch & 1, kk = ch >> 1;
         if (kk == 0) {
@@ -271,6 +299,8 @@ struct Attn8 {
       __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // VMEM reads
       __builtin_amdgcn_sched_barrier(0);
     }
+    // rounded sum of tile t-1 (shift of step t-1), then both it and O move to this step's shift
+    lh = fmaf(rsum, pinvf[B ^ 1], lh) * alpha;
     // deferred correction of O for rows whose shift moved
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
@@ -288,6 +318,7 @@ struct Attn8 {
       const i32x8 a = ch == 0 ? vop[0] : read_v(slot, ch);
       oacc[ch] = mfma_fp8_bs(a, pbuf[B], oacc[ch], pscale[B]);
     }
+    lh = fmaf(rounded_sum(pbuf[B]), pinvf[B], lh);
   }
 };
 
@@ -299,6 +330,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
     uint32_t qand) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   Attn8<CAUSAL> s;
+  // work item -> (query block, head): heaviest causal blocks first, heads interleaved
+  // (longest first balances the compute units; grouping each XCD's heads one after
+  // another read only the algorithmic HBM bytes but ran 7 % slower)
   const int L = blockIdx.x;
   const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
   const int bh = L % BH;
@@ -364,6 +398,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   }
   s.m = -kInf;
   s.l = 0.f;
+  s.lh = 0.f;
   s.alpha = 1.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -384,6 +419,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   }
   s.pbuf[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   s.pscale[1] = 127;
+  s.pinvf[1] = 0.f;
+  {
+    // selector: lane l supplies A row l % 16, codes 8 (l / 16) .. + 7; row 4 G' is one
+    // (e4m3 0x38) in the lane groups G with G % 2 == G' % 2
+    const int row = s.lane & 15, grp = s.lane >> 4;
+    s.sel = (row % 4 == 0 && (row / 4) % 2 == grp % 2) ? (long)0x3838383838383838ull : 0l;
+  }
   __syncthreads();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -423,10 +465,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   if ((nT - 1) & 1) s.template last_pv<1>((nT - 1) % kSlots);
   else s.template last_pv<0>((nT - 1) % kSlots);
 
-  // ---- epilogue: O = acc * svmax / sum, LSE = ln 2 * (m + log2(sum) - 6)
+  // ---- epilogue: O = acc * svmax / (rounded sum), LSE = ln 2 * (m + log2(sum) - 6).  The
+  // rounded sum already covers both lanes of a query; l is this lane's half of the sum.
   const float lt = sum_pair(s.l);
   if (qi < N) {
-    const float inv = s.svmax / lt;
+    const float inv = s.svmax / s.lh;
 #pragma unroll
     for (int db = 0; db < 4; ++db) store_row_bf16(o + base + (size_t)qi * kD + db * 32, s.oacc[db], inv, s.g);
     if (s.g == 0) lse[(size_t)bh * N + qi] = (s.m + log2_fast(lt) - kPShift) * kLn2;

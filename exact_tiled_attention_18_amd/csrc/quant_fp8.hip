@@ -11,7 +11,8 @@
 // fp32 registers; the 1/sqrt(d) factor is folded into the tile scale.  A tile
 // is 128 consecutive rows of one (batch, head) with all d columns; its scale
 // is amax / 448 and every value is divided by it and rounded to the nearest
-// e4m3 code (ties to even; the largest magnitude maps to 448).
+// e4m3 code (ties to even; the largest magnitude maps to 448); a tile of
+// magnitudes below 2^-96 counts as all-zero (scale 1).
 //
 // One workgroup quantises one tile: it reads the tile once (bf16), keeps it
 // in registers through the transform and the amax reduction, and writes the
@@ -27,6 +28,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileRows = 128;
+// A tile whose largest magnitude (after the unnormalised transform) is below 2^-96
+// is quantised as an all-zero tile: scale 1, every code +-0.  Above it, 448 / amax
+// stays finite (below 2^105) and the scale amax / (448 sqrt(d)) a normal fp32 value;
+// without the bound a tile of tiny values (bf16 subnormals, say) would get an
+// infinite multiplier and turn its zero entries into NaN codes.
+constexpr float kMinAmax = 0x1p-96f;
 
 // four fp32 -> four OCP e4m3 codes packed in 32 bits (v_cvt_pk_fp8_f32: round to
 // nearest even).  The scaled values here satisfy |t| <= 448 up to one rounding
@@ -136,10 +143,11 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
   // value / scale = z * 448 / amax(z): the rotation's 1/sqrt(d) cancels here
-  const float mult = amax > 0.f ? 448.0f / amax : 1.0f;
+  const bool live = amax >= kMinAmax;
+  const float mult = live ? 448.0f / amax : 1.0f;
   if (tid == 0) {
     const float den = ROTATE ? 448.0f * __builtin_sqrtf((float)D) : 448.0f;
-    x_scale[(size_t)bh * nTiles + tile] = amax > 0.f ? amax / den : 1.0f;
+    x_scale[(size_t)bh * nTiles + tile] = live ? amax / den : 1.0f;
   }
 
 #pragma unroll
@@ -217,8 +225,9 @@ __global__ __launch_bounds__(kThreads) void quant_transpose_kernel(
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float mult = amax > 0.f ? 448.0f / amax : 1.0f;
-  if (tid == 0) x_scale[(size_t)bh * nTiles + tile] = amax > 0.f ? amax / 448.0f : 1.0f;
+  const bool live = amax >= kMinAmax;
+  const float mult = live ? 448.0f / amax : 1.0f;
+  if (tid == 0) x_scale[(size_t)bh * nTiles + tile] = live ? amax / 448.0f : 1.0f;
 
   const int pos = R * j;  // byte position of this thread's rows in a column row
   const int off = (((pos >> 4) ^ (cg & 7)) << 4) + (pos & 15);

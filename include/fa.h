@@ -61,14 +61,23 @@ enum fa_status {
 
 enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
 
-/* Version of this interface (FA_ABI_VERSION). */
+/* Version of this interface (FA_ABI_VERSION).  The pages define no interface;
+ * the version lets a caller check the layout of the calls below. */
 int fa_abi_version(void);
 
-/* Static, human-readable name of a status code ("unknown status" otherwise). */
+/* Static, human-readable name of a status code ("unknown status" otherwise);
+ * the codes are the validation results listed with each call below. */
 const char* fa_status_string(int status);
 
 /*
- * fa_fwd -- attention forward in fp32 or bf16.
+ * fa_fwd -- attention forward in fp32 or bf16: the exact, IO-aware tiled
+ * forward pass of page "FlashAttention-Skalierung, Multi-GPU-Training und
+ * Gewichtsquantisierung", section 1, FlashAttention-2 items (the online
+ * softmax with its rescaling moved to the end of the inner loop; the outer
+ * loop over query blocks and the inner loop over K/V tiles, with the work of
+ * one head spread over the sequence), also the FlashAttention-2 wiki page,
+ * section "Technische Architektur und Funktionsprinzipien", items 1 and 2;
+ * it returns O and the row logsumexp.
  *   q, k, v : [B, H, N, d] of `dtype` (FA_F32: float32, FA_BF16: bfloat16).
  *   o       : [B, H, N, d] of `dtype`, fully overwritten.
  *   lse     : float32 [B, H, N], fully overwritten.
@@ -101,8 +110,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *             beyond holding code 0 (the layout fa_fwd_fp8 wants for V).
  *   x_scale : float32 [B, H, ceil(N/128)]: one scale per tile of 128 rows
  *             (the last tile may be partial) = max |value| over the tile / 448,
- *             or 1 for an all-zero tile.  code = e4m3(value / scale), rounded
- *             to nearest even and saturated at +-448.
+ *             or 1 for an all-zero tile -- a tile whose largest magnitude is
+ *             below 2^-96 (of the rotated values times sqrt(d) with signs)
+ *             counts as all-zero.  code = e4m3(value / scale), rounded to
+ *             nearest even and saturated at +-448.
  *   d       : 64 or 128.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, transpose_out),
  * FA_ERR_ALIAS, FA_ERR_HIP.
@@ -112,7 +123,14 @@ int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t
                         void* stream);
 
 /*
- * fa_fwd_fp8 -- attention forward on e4m3 operands with per-tile scales.
+ * fa_fwd_fp8 -- attention forward on e4m3 operands with per-tile scales: the
+ * FP8 variant of the pages (page "FlashAttention-Skalierung, Multi-GPU-
+ * Training und Gewichtsquantisierung", section 1, FlashAttention-3 FP8 item:
+ * FP8 matrix products at twice the raw rate of 16-bit ones, kept accurate by
+ * block quantisation with one scale per small tile and by the random
+ * orthogonal rotation of Q and K that fa_quant_rotate_fp8 applies; the news
+ * article on FlashAttention-3, section "Innovationen von FlashAttention-3",
+ * third item), computed with the same tiled online softmax as fa_fwd.
  *   q8, k8  : e4m3 codes [B, H, N, d] from fa_quant_rotate_fp8 with the same signs.
  *   v8      : e4m3 codes of V (not rotated); v_transposed must be 1 and v8
  *             laid out [B, H, d, FA_FP8_VT_COLS(N)] with zero codes in the
@@ -124,8 +142,9 @@ int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t
  * a (query tile, key tile) pair is multiplied by scale * q_scale * k_scale;
  * the probabilities of a key tile are multiplied by 2^6 * v_scale / (largest
  * v_scale of the head) and rounded to e4m3 for the P V product (the factors
- * are divided out at the end); the row sums use the unrounded fp32
- * probabilities.
+ * are divided out at the end); O is normalised by the sum of those rounded
+ * probabilities (the weights the P V product used), LSE by the sum of the
+ * unrounded fp32 ones.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, v_transposed,
  * causal), FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP.
  */

@@ -14,6 +14,9 @@ DESIGN.md:
   saturates to +-448;
 * tile: 128 consecutive rows of one (batch, head), all d columns; its scale is
   amax / 448 (1 when the tile is all zero), so the largest entry maps to +-448;
+  a tile whose amax is below 2^-96 (2^-96 / sqrt(d) for a rotated tile, whose
+  device transform leaves out the 1/sqrt(d)) is treated as all zero -- scale 1,
+  so its values round to codes of zero -- which keeps 448 / amax finite;
 * rotation: the same R = diag(s) H_d / sqrt(d) for Q and K (H_d the Sylvester
   Hadamard matrix in natural order, s a random +-1 vector), which leaves
   Q K^T unchanged because R R^T = I; V is not rotated;
@@ -101,12 +104,17 @@ def rotate(x, signs) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # block quantisation
 # ----------------------------------------------------------------------------
-def quantize_tiles(y, tile: int = TILE_ROWS):
+MIN_AMAX = 2.0 ** -96  # below this a tile counts as all zero
+
+
+def quantize_tiles(y, tile: int = TILE_ROWS, min_amax: float = MIN_AMAX):
     """Per-tile e4m3 quantisation of y ([B, H, N, d], float64).
 
     Returns (codes uint8 [B,H,N,d], scales float64 [B,H,ceil(N/tile)],
     t float64 [B,H,N,d]) where t = y / scale is the exact value that was
     rounded to a code (used to recognise rounding ties in comparisons).
+    A tile with amax < min_amax gets scale 1 (its values, all below 2^-96,
+    then round to codes of zero).
     """
     y = np.asarray(y, dtype=np.float64)
     B, H, N, d = y.shape
@@ -116,15 +124,19 @@ def quantize_tiles(y, tile: int = TILE_ROWS):
     for i in range(nt):
         blk = y[:, :, i * tile:(i + 1) * tile, :]
         amax = np.abs(blk).max(axis=(2, 3))
-        sc = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+        sc = np.where(amax >= min_amax, amax / E4M3_MAX, 1.0)
         scales[:, :, i] = sc
         t[:, :, i * tile:(i + 1) * tile, :] = blk / sc[:, :, None, None]
     return e4m3_encode(t), scales, t
 
 
 def quantize_rotate(x, signs, tile: int = TILE_ROWS):
-    """Rotate (when signs is not None) then block-quantise; see quantize_tiles."""
-    return quantize_tiles(rotate(x, signs), tile)
+    """Rotate (when signs is not None) then block-quantise; see quantize_tiles.
+    The zero-tile bound applies to the unnormalised transform x diag(s) H_d,
+    i.e. to sqrt(d) times the rotated values."""
+    y = rotate(x, signs)
+    bound = MIN_AMAX if signs is None else MIN_AMAX / np.sqrt(y.shape[-1])
+    return quantize_tiles(y, tile, bound)
 
 
 def dequantize(codes, scales, tile: int = TILE_ROWS) -> np.ndarray:

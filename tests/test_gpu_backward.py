@@ -62,14 +62,18 @@ def test_backward_small(fa, shape, causal):
     assert max(e) <= TOL and max(x) <= TOL
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [0.0, -0.15, 0.5])
-def test_backward_scales(fa, scale):
-    B, H, N, d = 1, 2, 200, 128
-    G.log(f"case backward scale={scale}")
+def test_backward_scales(fa, scale, d, causal):
+    """Zero, negative and large scales, both head sizes (the d = 64 kernels flip or zero
+    Q's bits, the pipelined d = 128 dK/dV kernel takes a signed multiplier)."""
+    B, H, N = 1, 2, 200
+    G.log(f"case backward scale={scale} d={d} causal={causal}")
     q, k, v = synthetic.draw_qkv(B, H, N, d, seed=31, dtype="bf16")
     do = synthetic.draw_qkv(B, H, N, d, seed=32, dtype="bf16")[0]
-    got, o = _grads(fa, q, k, v, do, True, scale, with_o=True)
-    ref = A.backward(q, k, v, do, True, scale, o=o)
+    got, o = _grads(fa, q, k, v, do, causal, scale, with_o=True)
+    ref = A.backward(q, k, v, do, causal, scale, o=o)
     if scale == 0.0:  # S does not depend on Q or K: their gradients vanish
         assert not got[0].float().abs().max().item() and not got[1].float().abs().max().item()
         e = _errors(got[2:], ref[2:])
@@ -77,6 +81,23 @@ def test_backward_scales(fa, scale):
         e = _errors(got, ref)
     G.log(f"  normwise errors {['%.2e' % x for x in e]}")
     assert max(e) <= TOL
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_zero_scale_overflowing_scores(fa, d):
+    """scale 0 with |Q K^T| beyond the fp32 range: the scores are 0 by definition, so
+    every gradient is finite, dQ = dK = 0 and dV = P^T dO with uniform P."""
+    G.log(f"case backward zero scale, overflowing Q K^T, d={d}")
+    q, k, v = synthetic.draw_qkv(1, 2, 100, d, seed=33, dtype="bf16")
+    q, k = (q.float() * 2.0 ** 70).to(torch.bfloat16), (k.float() * 2.0 ** 70).to(torch.bfloat16)
+    do = synthetic.draw_qkv(1, 2, 100, d, seed=34, dtype="bf16")[0]
+    for causal in (False, True):
+        got, o = _grads(fa, q, k, v, do, causal, 0.0, with_o=True)
+        assert all(bool(torch.isfinite(g.float()).all()) for g in got)
+        assert not got[0].float().abs().max().item() and not got[1].float().abs().max().item()
+        e = _errors(got[2:], A.backward(q, k, v, do, causal, 0.0, o=o)[2:])
+        G.log(f"  causal={causal} dV normwise error {e[0]:.2e}")
+        assert max(e) <= TOL
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -164,6 +164,31 @@ def test_quantizer_small(fa, N, d):
             assert nb <= 1e-2 * nt
 
 
+@pytest.mark.parametrize("rot", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantizer_tiny_tile(fa, d, rot):
+    """A tile of bf16 subnormals (magnitudes below 2^-96) quantises as an all-zero tile
+    (scale 1, codes of zero, no NaN codes); the next tile, at 2^-90, keeps the amax rule."""
+    G.log(f"case quantizer tiny tile d={d} rotate={rot}")
+    x = torch.linspace(-1, 1, 256 * d, dtype=torch.float64).reshape(1, 1, 256, d)
+    x[:, :, :128] *= 2.0 ** -130
+    x[:, :, 128:] *= 2.0 ** -90
+    x = x.to(torch.bfloat16)
+    signs = synthetic.draw_signs(d, 5)
+    sg = torch.from_numpy(signs).to(DEV) if rot else None
+    for tr in (False, True):
+        x8, xs = fa.fa_quant_rotate_fp8(x.to(DEV), sg, tr)
+        torch.cuda.synchronize()
+        c = x8.cpu()
+        c = c[..., :256].transpose(-1, -2) if tr else c
+        assert float(xs[0, 0, 0]) == 1.0 and bool(((c[0, 0, :128] & 0x7F) == 0).all())
+        assert not bool(((c & 0x7F) == 0x7F).any())  # no NaN code anywhere
+        assert 0.0 < float(xs[0, 0, 1]) < 1e-20
+        live = (x8[..., 128:256].contiguous(), x8[:, :, 128:]) [0 if tr else 1]
+        nb, nt = G.check_codes(live, xs[:, :, 1:], x[:, :, 128:], signs if rot else None, transposed=tr)
+        assert nb <= 1e-2 * nt
+
+
 @pytest.mark.parametrize("outliers", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 100, 128, 200, 256, 640])

@@ -132,6 +132,27 @@ def test_zero_tile_gets_unit_scale():
     assert scales[0, 0, 1] == 3.0 / 448
 
 
+def test_tiny_tile_counts_as_zero():
+    """A tile of magnitudes below 2^-96 (bf16 subnormals here) gets scale 1 and codes of
+    zero (448 / amax would overflow fp32); one just above keeps the amax / 448 rule."""
+    y = np.zeros((1, 1, 256, 8))
+    y[0, 0, :128] = np.linspace(-1, 1, 128 * 8).reshape(128, 8) * 2.0 ** -130
+    y[0, 0, 128:] = np.linspace(-1, 1, 128 * 8).reshape(128, 8) * 2.0 ** -90
+    codes, scales, _ = F.quantize_tiles(y)
+    assert scales[0, 0, 0] == 1.0 and np.all((codes[0, 0, :128] & 0x7F) == 0)
+    assert scales[0, 0, 1] == 2.0 ** -90 / 448 and np.isfinite(448 / (2.0 ** -90))
+    assert np.all(np.isfinite(F.dequantize(codes, scales)))
+    assert (codes[0, 0, 255, 7] & 0x7F) == 0x7E  # the amax element still maps to 448
+    # the rotated path applies the bound to the unnormalised transform (sqrt(d) x larger)
+    s = np.ones(8, dtype=np.int8)
+    x = np.zeros((1, 1, 128, 8)); x[0, 0, 0, 0] = 2.0 ** -97  # transform amax 2^-97 < 2^-96
+    c, sc, _ = F.quantize_rotate(x, s)
+    assert sc[0, 0, 0] == 1.0 and np.all((c & 0x7F) == 0)
+    x[0, 0, 0, 0] = 2.0 ** -95
+    c, sc, _ = F.quantize_rotate(x, s)
+    assert sc[0, 0, 0] == pytest.approx(2.0 ** -95 / np.sqrt(8) / 448, rel=1e-12)
+
+
 def test_mirrored_oracle_is_exact_on_representable_inputs():
     """Inputs that are e4m3 values times a tile scale quantise losslessly,
     so the mirrored oracle must equal the exact one there."""

@@ -18,7 +18,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
-FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP = range(7)
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_SCRATCH = range(8)
+FA_BWD_NOALLOC_MAX_ROWS = 1 << 22  # rows (B * H * N) of fa_bwd_noalloc's static workspace
 FA_F32, FA_BF16 = 0, 1
 TILE_ROWS = 128  # rows per fp8 quantisation tile
 
@@ -61,6 +62,8 @@ def load_library():
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_bwd.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i64, i64, i64, i64, i32, f32, i32, vp]
+    lib.fa_bwd_noalloc.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_merge.restype = i32
     lib.fa_merge.argtypes = [vp, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp]
     _lib = lib
@@ -281,4 +284,25 @@ def fa_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = No
     lib = load_library()
     _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                       _ptr(delta), B, H, N, d, int(causal), float(scale), FA_BF16, _stream(stream)))
+    return dq, dk, dv
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, dq=None, dk=None,
+                   dv=None, stream=None):
+    """fa_bwd with the library's static workspace instead of a delta argument (the C call
+    allocates nothing; outputs are allocated here unless passed).  Calls that overlap on
+    one GPU share that workspace and race."""
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_dense(q, k, v, o, dout, lse, dq, dk, dv)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _expect(t, (B, H, N, d), torch.bfloat16, name)
+    _expect(lse, (B, H, N), torch.float32, "lse")
+    lib = load_library()
+    _check(lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, H, N, d, int(causal), float(scale), FA_BF16, _stream(stream)))
     return dq, dk, dv

@@ -2,6 +2,7 @@
 // Validation never touches the GPU, so a rejected call has no side effect.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "launch.h"
@@ -38,6 +39,29 @@ bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// fa_bwd_noalloc's workspace: one static array per GPU (each device holds its own
+// copy, at its own address).  In host code `scratch` names a host-side stand-in,
+// not device memory, so the kernels only ever get the device address looked up
+// below, one per device.
+__device__ __align__(256) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch` (looked up once per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -53,6 +77,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "non-finite scale";
     case FA_ERR_ALIAS: return "output overlaps input";
     case FA_ERR_HIP: return "HIP launch error";
+    case FA_ERR_SCRATCH: return "problem exceeds the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -211,6 +236,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   const fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, N, d, causal, scale,
                       static_cast<hipStream_t>(stream)};
   return hip_status(fa::launch_attn_bwd(a));
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                   int causal, float scale, int dtype, void* stream) {
+  int64_t n = 0;
+  if (int st = shape_status(B, H, N, d, &n)) return st;
+  if (B * H * N > FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_SCRATCH;
+  // the argument checks that need no workspace, before the device is touched
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (n == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  void* ws = nullptr;
+  if (int st = scratch_address(&ws)) return st;
+  // the workspace is library memory, so it overlaps none of the caller's buffers
+  return fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(ws), B, H, N, d, causal, scale, dtype,
+                stream);
 }
 
 }  // extern "C"

@@ -31,7 +31,8 @@
  *  - Input values are not inspected; non-finite inputs propagate.
  *  - Results are bitwise repeatable for the same inputs, shape and device
  *    (no atomics, fixed reduction order).
- *  - Calls are reentrant; the library holds no mutable state.
+ *  - Calls are reentrant; the library holds no mutable state (except
+ *    fa_bwd_noalloc's static scratch, described there).
  */
 #ifndef FA_H_
 #define FA_H_
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 /* Row length (keys) of transposed V codes: N rounded up to a multiple of 64. */
 #define FA_FP8_VT_COLS(N) ((((N) + 63) / 64) * 64)
@@ -56,8 +57,13 @@ enum fa_status {
   FA_ERR_UNSUPPORTED = 3, /* head dim, dtype, flag or layout not provided      */
   FA_ERR_SCALE = 4,       /* scale is NaN or infinite                          */
   FA_ERR_ALIAS = 5,       /* an output overlaps an input                       */
-  FA_ERR_HIP = 6          /* the HIP runtime rejected a launch                 */
+  FA_ERR_HIP = 6,         /* the HIP runtime rejected a launch                 */
+  FA_ERR_SCRATCH = 7      /* the problem needs more than the library's static  */
+                          /* scratch (fa_bwd_noalloc: B * H * N rows)          */
 };
+
+/* Rows (B * H * N) that fa_bwd_noalloc's static scratch holds: 16 MiB of fp32. */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 22)
 
 enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
 
@@ -234,6 +240,27 @@ int fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
            int64_t N, int64_t d, int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving or training loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, with the row-sum workspace
+ * `delta` taken from a static device array of FA_BWD_NOALLOC_MAX_ROWS floats
+ * (16 MiB per GPU, held until the process ends) instead of an argument.
+ *   Arguments: as fa_bwd, without delta.
+ *   The call allocates nothing (no hipMalloc, hipFree or allocating library
+ *   routine).  Its first call on a device looks up that device's copy of the
+ *   array (hipGetSymbolAddress, with the device current).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (on different streams, or from several threads) race and give wrong
+ *   gradients; calls one after another on a stream are safe.  The array needs
+ *   no clearing: each call overwrites the rows it reads.
+ * Errors: those of fa_bwd, and FA_ERR_SCRATCH when B * H * N exceeds
+ * FA_BWD_NOALLOC_MAX_ROWS (checked before any pointer or device access).
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                   int64_t N, int64_t d, int causal, float scale, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,8 +28,9 @@ def fa():
 
 
 def test_header_declares_the_api():
-    assert _declared_functions() == ["fa_abi_version", "fa_bwd", "fa_fwd", "fa_fwd_fp8", "fa_fwd_partial",
-                                     "fa_fwd_split", "fa_merge", "fa_quant_rotate_fp8", "fa_status_string"]
+    assert _declared_functions() == ["fa_abi_version", "fa_bwd", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_fp8",
+                                     "fa_fwd_partial", "fa_fwd_split", "fa_merge", "fa_quant_rotate_fp8",
+                                     "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -39,8 +40,9 @@ def test_library_exports_every_declared_symbol(fa):
 
 
 def test_version_and_status_strings(fa):
-    assert fa.fa_abi_version() == 3
+    assert fa.fa_abi_version() == 4
     assert fa.fa_status_string(0) == "ok"
+    assert fa.fa_status_string(fa.FA_ERR_SCRATCH) == "problem exceeds the library's static scratch"
     assert fa.fa_status_string(3) == "unsupported argument"
     assert fa.fa_status_string(99) == "unknown status"
 
@@ -187,3 +189,26 @@ def test_bwd_validation(fa):
     assert _bwd(fa, dk=ctypes.c_void_p(0x7C000000 + 32)) == fa.FA_ERR_ALIAS  # dk overlaps dq
     assert _bwd(fa, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None, delta=None,
                 N=0) == fa.FA_OK
+
+
+def _bwd_noalloc(fa, q=P, k=P2, v=P3, o=P4, do=P5, lse=ctypes.c_void_p(0x7A000000), dq=ctypes.c_void_p(0x7C000000),
+                 dk=ctypes.c_void_p(0x7E000000), dv=ctypes.c_void_p(0x80000000), B=1, H=1, N=128, d=64, causal=1,
+                 scale=0.125, dtype=1):
+    return fa.load_library().fa_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, causal, scale, dtype, None)
+
+
+def test_bwd_noalloc_validation(fa):
+    """Rejected before the device or any pointer is touched: a problem beyond the static
+    workspace (even with null pointers), and every argument error fa_bwd reports."""
+    rows = fa.FA_BWD_NOALLOC_MAX_ROWS
+    none = dict(q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None, dv=None)
+    assert _bwd_noalloc(fa, B=1, H=1, N=rows + 1, **none) == fa.FA_ERR_SCRATCH
+    assert _bwd_noalloc(fa, B=4, H=32, N=rows // 64, **none) == fa.FA_ERR_SCRATCH
+    assert _bwd_noalloc(fa, N=-1) == fa.FA_ERR_SHAPE
+    assert _bwd_noalloc(fa, d=32) == fa.FA_ERR_UNSUPPORTED
+    assert _bwd_noalloc(fa, dtype=0) == fa.FA_ERR_UNSUPPORTED
+    assert _bwd_noalloc(fa, causal=2) == fa.FA_ERR_UNSUPPORTED
+    assert _bwd_noalloc(fa, scale=float("nan")) == fa.FA_ERR_SCALE
+    assert _bwd_noalloc(fa, dv=None) == fa.FA_ERR_NULL
+    assert _bwd_noalloc(fa, N=0, **none) == fa.FA_OK
+

@@ -54,8 +54,12 @@ def load_library():
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_quant_rotate_fp8.restype = i32
     lib.fa_quant_rotate_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.fa_quant_rotate_fp8_tensor.restype = i32
+    lib.fa_quant_rotate_fp8_tensor.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.fa_fwd_fp8.restype = i32
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, f32, vp]
+    lib.fa_fwd_fp8_pbf16.restype = i32
+    lib.fa_fwd_fp8_pbf16.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, f32, vp]
     lib.fa_fwd_partial.restype = i32
     lib.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_fwd_split.restype = i32
@@ -125,8 +129,11 @@ def fa_fwd(q, k, v, causal: bool = False, scale: float | None = None, o=None, ls
     return o, lse
 
 
-def fa_quant_rotate_fp8(x, signs=None, transpose_out: bool = False, x8=None, x_scale=None, stream=None):
-    """e4m3 codes (uint8) and per-128-row-tile scales of x (bfloat16 [B, H, N, d])."""
+def fa_quant_rotate_fp8(x, signs=None, transpose_out: bool = False, x8=None, x_scale=None, stream=None,
+                        per_tensor: bool = False):
+    """e4m3 codes (uint8) and per-128-row-tile scales of x (bfloat16 [B, H, N, d]); with
+    per_tensor, one scale for the whole tensor, repeated in every tile entry
+    (fa_quant_rotate_fp8_tensor)."""
     B, H, N, d = x.shape
     x8_shape = (B, H, d, vt_cols(N)) if transpose_out else (B, H, N, d)
     if x8 is None:
@@ -140,14 +147,15 @@ def fa_quant_rotate_fp8(x, signs=None, transpose_out: bool = False, x8=None, x_s
     if signs is not None:
         _expect(signs, (d,), torch.int8, "signs")
     lib = load_library()
-    _check(lib.fa_quant_rotate_fp8(_ptr(x), _ptr(x8), _ptr(x_scale), _ptr(signs), B, H, N, d,
-                                   int(transpose_out), _stream(stream)))
+    fn = lib.fa_quant_rotate_fp8_tensor if per_tensor else lib.fa_quant_rotate_fp8
+    _check(fn(_ptr(x), _ptr(x8), _ptr(x_scale), _ptr(signs), B, H, N, d, int(transpose_out), _stream(stream)))
     return x8, x_scale
 
 
 def fa_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
-               o=None, lse=None, stream=None):
-    """O (bfloat16), LSE from e4m3 Q, K ([B, H, N, d]) and transposed V ([B, H, d, vt_cols(N)])."""
+               o=None, lse=None, stream=None, p_bf16: bool = False):
+    """O (bfloat16), LSE from e4m3 Q, K ([B, H, N, d]) and transposed V ([B, H, d, vt_cols(N)]);
+    with p_bf16, the probabilities stay in bf16 for P V (fa_fwd_fp8_pbf16)."""
     B, H, N, d = q8.shape
     if scale is None:
         scale = 1.0 / d ** 0.5
@@ -165,19 +173,22 @@ def fa_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, sca
     _expect(o, (B, H, N, d), torch.bfloat16, "o")
     _expect(lse, (B, H, N), torch.float32, "lse")
     lib = load_library()
-    _check(lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), 1,
-                          _ptr(o), _ptr(lse), B, H, N, d, int(causal), float(scale), _stream(stream)))
+    fn = lib.fa_fwd_fp8_pbf16 if p_bf16 else lib.fa_fwd_fp8
+    _check(fn(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), 1, _ptr(o), _ptr(lse),
+              B, H, N, d, int(causal), float(scale), _stream(stream)))
     return o, lse
 
 
-def fp8_attention(q, k, v, signs, causal: bool = False, scale: float | None = None, stream=None):
+def fp8_attention(q, k, v, signs, causal: bool = False, scale: float | None = None, stream=None,
+                  per_tensor: bool = False, p_bf16: bool = False):
     """The FP8 path end to end: three pre-pass calls (Q and K rotated with the
     same signs, V not rotated and written transposed) and the fp8 forward.
-    Returns (o, lse, (q8, k8, v8t, q_scale, k_scale, v_scale))."""
-    q8, qs = fa_quant_rotate_fp8(q, signs, False, stream=stream)
-    k8, ks = fa_quant_rotate_fp8(k, signs, False, stream=stream)
-    v8t, vs = fa_quant_rotate_fp8(v, None, True, stream=stream)
-    o, lse = fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale, stream=stream)
+    per_tensor and p_bf16 select the ablation variants (one scale per tensor;
+    probabilities in bf16).  Returns (o, lse, (q8, k8, v8t, q_scale, k_scale, v_scale))."""
+    q8, qs = fa_quant_rotate_fp8(q, signs, False, stream=stream, per_tensor=per_tensor)
+    k8, ks = fa_quant_rotate_fp8(k, signs, False, stream=stream, per_tensor=per_tensor)
+    v8t, vs = fa_quant_rotate_fp8(v, None, True, stream=stream, per_tensor=per_tensor)
+    o, lse = fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale, stream=stream, p_bf16=p_bf16)
     return o, lse, (q8, k8, v8t, qs, ks, vs)
 
 

@@ -103,8 +103,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return hip_status(dtype == FA_F32 ? fa::launch_attn_f32(a) : fa::launch_attn_bf16(a));
 }
 
-int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t* signs, int64_t B,
-                        int64_t H, int64_t N, int64_t d, int transpose_out, void* stream) {
+}  // extern "C"
+
+namespace {
+int quant_rotate(const void* x, uint8_t* x8, float* x_scale, const int8_t* signs, int64_t B, int64_t H, int64_t N,
+                 int64_t d, int transpose_out, void* stream, int per_tensor) {
   int64_t n = 0;
   if (int st = shape_status(B, H, N, d, &n)) return st;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -118,13 +121,30 @@ int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t
     return FA_ERR_ALIAS;
   if (signs && (overlaps(x8, xb, signs, d) || overlaps(x_scale, sb, signs, d))) return FA_ERR_ALIAS;
 
-  const fa::QuantArgs a{x, x8, x_scale, signs, B, H, N, d, transpose_out, static_cast<hipStream_t>(stream)};
+  const fa::QuantArgs a{x, x8, x_scale, signs, B, H, N, d, transpose_out, static_cast<hipStream_t>(stream),
+                        per_tensor};
   return hip_status(fa::launch_quant_rotate_fp8(a));
 }
+}  // namespace
 
-int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
-               const float* k_scale, const float* v_scale, int v_transposed, void* o, float* lse,
-               int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale, void* stream) {
+extern "C" {
+
+int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t* signs, int64_t B,
+                        int64_t H, int64_t N, int64_t d, int transpose_out, void* stream) {
+  return quant_rotate(x, x8, x_scale, signs, B, H, N, d, transpose_out, stream, 0);
+}
+
+int fa_quant_rotate_fp8_tensor(const void* x, uint8_t* x8, float* x_scale, const int8_t* signs, int64_t B,
+                               int64_t H, int64_t N, int64_t d, int transpose_out, void* stream) {
+  return quant_rotate(x, x8, x_scale, signs, B, H, N, d, transpose_out, stream, 1);
+}
+
+}  // extern "C"
+
+namespace {
+int fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale, const float* k_scale,
+            const float* v_scale, int v_transposed, void* o, float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+            int causal, float scale, void* stream, int p_bf16) {
   int64_t n = 0;
   if (int st = shape_status(B, H, N, d, &n)) return st;
   if (d != 128 || v_transposed != 1) return FA_ERR_UNSUPPORTED;
@@ -146,8 +166,23 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const fl
   if (overlaps(o, ob, lse, lb)) return FA_ERR_ALIAS;
 
   const fa::Fp8AttnArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale,
-                          static_cast<hipStream_t>(stream)};
+                          static_cast<hipStream_t>(stream), p_bf16};
   return hip_status(fa::launch_attn_fp8(a));
+}
+}  // namespace
+
+extern "C" {
+
+int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+               const float* k_scale, const float* v_scale, int v_transposed, void* o, float* lse,
+               int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale, void* stream) {
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, v_transposed, o, lse, B, H, N, d, causal, scale, stream, 0);
+}
+
+int fa_fwd_fp8_pbf16(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                     const float* k_scale, const float* v_scale, int v_transposed, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale, void* stream) {
+  return fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, v_transposed, o, lse, B, H, N, d, causal, scale, stream, 1);
 }
 
 int fa_fwd_split(const void* q, const void* k, const void* v, float* o_parts, float* lse_parts, int64_t B,

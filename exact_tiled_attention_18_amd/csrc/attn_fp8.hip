@@ -476,10 +476,229 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_fp8_kernel(
   }
 }
 
+// ---- The same attention with the probabilities kept in bf16: S = Q8 K8^T on the fp8
+// matrix core as above, but P is rounded to bf16 and O += P V runs on the bf16 matrix
+// core (v_mfma_f32_32x32x16_bf16), with V's e4m3 codes widened to bf16 -- exactly, as
+// every e4m3 value is a bf16 value -- when its tile is staged into LDS.  This is the
+// accuracy reference for the rounding of P to e4m3: the two kernels differ only
+// there (and in the P V instruction).  It is written plainly, without the software
+// pipeline: one 64-key tile per step, two barriers per step, K8 and V8^T tiles
+// loaded one step ahead into registers.
+//
+// Layouts.  The scores come out as in Attn8 (lane half g holds keys 8g..8g+7 and
+// 16+8g..16+8g+7 of each 32-key half kb), which for k-step j = 2 kb + h of the bf16
+// product (keys 16 j .. 16 j + 15) is exactly the B-operand layout of P^T: lane
+// half g needs keys 16 j + 8 g .. + 7, i.e. registers 8 h .. 8 h + 7 of half kb.
+// V^T is kept row-major in LDS, one d-row of 64 keys (bf16) per row, so the A
+// operand of a k-step (d-row 32 db + l % 32, keys 16 j + 8 (l / 32) .. + 7) is one
+// 16-byte read.  V's tile scale ratio r = v_scale / v_scale_max goes wholly into
+// the exponent shift: P = bf16(2^6 r p), so O accumulates in units of
+// v_scale_max / 2^6 as in the fp8 kernel.  O is normalised by the sum of the
+// bf16-rounded probabilities (divided by r per tile), LSE by the fp32 sum.
+namespace pbf16 {
+constexpr int kVS16 = kBc * 2 + 16;  // bf16 V^T row stride (bytes)
+constexpr int kVBytes = kD * kVS16;
+constexpr float kSlack16 = 2.f;
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+}  // namespace pbf16
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_fwd_fp8_pbf16_kernel(
+    const uint8_t* __restrict__ q8, const uint8_t* __restrict__ k8, const uint8_t* __restrict__ v8t,
+    const float* __restrict__ qs, const float* __restrict__ ks, const float* __restrict__ vs,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int BH, int N, int nQB, float c, uint32_t qxor,
+    uint32_t qand) {
+  using namespace pbf16;
+  __shared__ __attribute__((aligned(16))) char kt[kKSlot];
+  __shared__ __attribute__((aligned(16))) char vt[kVBytes];
+  const int L = blockIdx.x;
+  const int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
+  const int bh = L % BH;
+  const int nTiles = (N + kTile - 1) / kTile;
+  const int ldv = (N + kBc - 1) / kBc * kBc;
+  const size_t base = (size_t)bh * N * kD;
+  constexpr int kRsrcWord3 = 0x00020000;  // raw buffer access: reads past the end return zeros
+  const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(k8 + base), (short)0, N * kD, kRsrcWord3);
+  const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v8t + (size_t)bh * kD * ldv), (short)0, kD * ldv, kRsrcWord3);
+  const float* ks_head = ks + (size_t)bh * nTiles;
+  const float* vs_head = vs + (size_t)bh * nTiles;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, li = lane & 31;
+  const int q0 = qblk * kBr, qw0 = q0 + (tid >> 6) * 32, qi = qw0 + li;
+  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
+  const int nT = (kv_end + kBc - 1) / kBc;
+  // the wavefront's last tile holding a key one of its rows sees (wave-uniform)
+  const int last_w = __builtin_amdgcn_readfirstlane(
+      qw0 >= N ? -1 : (CAUSAL ? min(qw0 + 31, N - 1) : N - 1) / kBc);
+
+  float svmax;
+  {
+    float mx = 0.f;
+    for (int i = lane; i < nTiles; i += 64) mx = fmaxf(mx, vs_head[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    svmax = uniform(mx);
+  }
+  const float log2_svmax = uniform(log2_fast(svmax));
+  const float cq = uniform(c * qs[(size_t)bh * nTiles + min(qw0 / kTile, nTiles - 1)]);
+
+  i32x8 qf[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+    if (qi < N) {
+      const uint8_t* p = q8 + base + (size_t)qi * kD + kk * 64 + g * 32;
+      lo = *reinterpret_cast<const uint4*>(p);
+      hi = *reinterpret_cast<const uint4*>(p + 16);
+    }
+    lo = make_uint4((lo.x ^ qxor) & qand, (lo.y ^ qxor) & qand, (lo.z ^ qxor) & qand, (lo.w ^ qxor) & qand);
+    hi = make_uint4((hi.x ^ qxor) & qand, (hi.y ^ qxor) & qand, (hi.z ^ qxor) & qand, (hi.w ^ qxor) & qand);
+    qf[kk] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m = -kInf, l = 0.f, lh = 0.f;
+
+  // this thread's 16-byte pieces: K8 row tid/8, bytes 16 (tid%8); V8^T row tid/4, keys 16 (tid%4)
+  const int kst_off = (tid >> 3) * kKS + (tid & 7) * 16;
+  const int vrow = tid >> 2, vcol = (tid & 3) * 16;
+  const int krd_off = permuted_row(li) * kKS + g * 32;
+  auto load_k = [&](int t) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, t * kBc * kD + tid * 16, 0, 0));
+  };
+  auto load_v = [&](int t) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vrow * ldv + t * kBc + vcol, 0, 0));
+  };
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  uint4 sk = load_k(0), sv = load_v(0);
+  for (int t = 0; t < nT; ++t) {
+    __syncthreads();  // every wavefront is done with tile t-1
+    *reinterpret_cast<uint4*>(kt + kst_off) = sk;
+    {
+      // 16 codes -> 16 bf16 (exact), natural key order
+      const uint32_t c4[4] = {sv.x, sv.y, sv.z, sv.w};
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c4[i], 1.0f, false));
+        b[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c4[i], 1.0f, true));
+      }
+      char* pv = vt + vrow * kVS16 + vcol * 2;
+      *reinterpret_cast<uint4*>(pv) = make_uint4(b[0], b[1], b[2], b[3]);
+      *reinterpret_cast<uint4*>(pv + 16) = make_uint4(b[4], b[5], b[6], b[7]);
+    }
+    __syncthreads();
+    if (t + 1 < nT) {
+      sk = load_k(t + 1);
+      sv = load_v(t + 1);
+    }
+    if (t > last_w) continue;  // no key of this tile is visible to the wavefront's rows
+    // S^T of the tile: two 32-key halves kb, two 64-byte halves of d
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16 z = {};
+      sc[kb] = mfma_fp8(lds_read32(kt + krd_off + kb * 32 * kKS), qf[0], z);
+      sc[kb] = mfma_fp8(lds_read32(kt + krd_off + kb * 32 * kKS + 64), qf[1], sc[kb]);
+    }
+    // mask: register r of half kb holds key t*64 + 32 kb + (r & 7) + 8 g + 2 (r & 8)
+    const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - t * kBc - g * 8;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kb * 32 + (r & 7) + (r & 8) * 2 > lim) sc[kb][r] = -kInf;
+    // tile factors: multiplier, log2 of r = v_scale / v_scale_max
+    const int st = min(t * kBc / kTile, nTiles - 1);
+    const float cst = uniform(cq * ks_head[st]);
+    const float lr = uniform(log2_fast(vs_head[st]) - log2_svmax);
+    const float inv_r = uniform(exp2_fast(-lr));
+    float mx = -kInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    const float mt = cst * max_pair(mx);  // -inf when the row sees no key of the tile
+    const float m_new = mt > m + kSlack16 ? mt : m;
+    const float alpha = m_new == -kInf ? 1.f : exp2_fast(m - m_new);
+    m = m_new;
+    // 2^(cst s - m + 6 + log2 r): the scaled probability that enters bf16
+    const float msub = m_new == -kInf ? 0.f : m_new - kPShift - lr;
+    float rs = 0.f, hs = 0.f;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[kb][r] = exp2_fast(fmaf(sc[kb][r], cst, -msub));
+        rs += sc[kb][r];
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint4 wv;
+        wv.x = pack_bf16x2(sc[kb][8 * h + 0], sc[kb][8 * h + 1]);
+        wv.y = pack_bf16x2(sc[kb][8 * h + 2], sc[kb][8 * h + 3]);
+        wv.z = pack_bf16x2(sc[kb][8 * h + 4], sc[kb][8 * h + 5]);
+        wv.w = pack_bf16x2(sc[kb][8 * h + 6], sc[kb][8 * h + 7]);
+        pb[kb][h] = __builtin_bit_cast(bf16x8, wv);
+        hs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), ones, hs, false);
+        hs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), ones, hs, false);
+        hs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.z), ones, hs, false);
+        hs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), ones, hs, false);
+      }
+    }
+    l = l * alpha + rs * inv_r;
+    lh = lh * alpha + hs * inv_r;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    // O^T += V^T P^T over the tile's four 16-key steps
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + li) * kVS16 + (16 * j + 8 * g) * 2);
+        oacc[db] = mfma_bf16(a, pb[j >> 1][j & 1], oacc[db]);
+      }
+  }
+
+  // ---- epilogue: O = acc * svmax / (rounded sum), LSE = ln 2 * (m + log2(sum) - 6)
+  const float lt = sum_pair(l), lht = sum_pair(lh);
+  if (qi < N) {
+    const float inv = svmax / lht;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) store_row_bf16(o + base + (size_t)qi * kD + db * 32, oacc[db], inv, g);
+    if (g == 0) lse[(size_t)bh * N + qi] = (m + log2_fast(lt) - kPShift) * kLn2;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_fp8(const Fp8AttnArgs& a) {
   const int BH = (int)(a.B * a.H), N = (int)a.N;
+  if (a.p_bf16) {
+    const int nQB = (N + kBr - 1) / kBr;
+    const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
+    const uint32_t qxor = a.scale < 0.f ? 0x80808080u : 0u;
+    const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
+    if (a.causal)
+      hipLaunchKernelGGL((attn_fwd_fp8_pbf16_kernel<true>), dim3((unsigned)(nQB * BH)), dim3(kThreads), 0, a.stream,
+                         a.q8, a.k8, a.v8t, a.q_scale, a.k_scale, a.v_scale, static_cast<uint16_t*>(a.o), a.lse, BH,
+                         N, nQB, c, qxor, qand);
+    else
+      hipLaunchKernelGGL((attn_fwd_fp8_pbf16_kernel<false>), dim3((unsigned)(nQB * BH)), dim3(kThreads), 0,
+                         a.stream, a.q8, a.k8, a.v8t, a.q_scale, a.k_scale, a.v_scale, static_cast<uint16_t*>(a.o),
+                         a.lse, BH, N, nQB, c, qxor, qand);
+    return hipGetLastError();
+  }
   const int nQB = (N + kBr - 1) / kBr;
   const dim3 grid((unsigned)(nQB * BH)), block(kThreads);
   // positive multiplier: negate Q (flip every code's sign bit) for a negative scale,

@@ -73,6 +73,7 @@ struct QuantArgs {
   int64_t B, H, N, d;
   int transpose_out;
   hipStream_t stream;
+  int per_tensor;  // 1: one scale (the whole tensor's amax) in every tile entry
 };
 hipError_t launch_quant_rotate_fp8(const QuantArgs& a);
 
@@ -89,6 +90,7 @@ struct Fp8AttnArgs {
   int causal;
   float scale;
   hipStream_t stream;
+  int p_bf16;  // 1: probabilities in bf16, P V on the bf16 matrix core
 };
 hipError_t launch_attn_fp8(const Fp8AttnArgs& a);
 

@@ -35,6 +35,14 @@ constexpr int kTileRows = 128;
 // infinite multiplier and turn its zero entries into NaN codes.
 constexpr float kMinAmax = 0x1p-96f;
 
+// Scale granularity (template MODE of the kernels below).  PER_TILE: each workgroup
+// quantises its tile with the tile's own amax.  AMAX: it only writes the tile's amax
+// into x_scale.  GIVEN: it quantises with the amax found in its x_scale entry (the
+// whole tensor's, spread there by reduce_amax_kernel) and replaces it by the scale.
+// AMAX, reduce, GIVEN is the per-tensor quantisation the block scales are compared
+// against.
+enum { PER_TILE = 0, AMAX = 1, GIVEN = 2 };
+
 // four fp32 -> four OCP e4m3 codes packed in 32 bits (v_cvt_pk_fp8_f32: round to
 // nearest even).  The scaled values here satisfy |t| <= 448 up to one rounding
 // of the multiplier, far below 464, the first value that would not round to
@@ -69,7 +77,7 @@ __device__ __forceinline__ void butterfly(float (&z)[8], int cg) {
   for (int e = 0; e < 8; ++e) z[e] = fmaf(z[e], sgn, partner<HM>(z[e]));
 }
 
-template <int D, bool ROTATE, bool TRANSPOSE>
+template <int D, bool ROTATE, bool TRANSPOSE, int MODE>
 __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ x8, float* __restrict__ x_scale,
     const int8_t* __restrict__ signs, int N, int nTiles) {
@@ -139,8 +147,13 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
+  if constexpr (MODE == GIVEN) amax = x_scale[(size_t)bh * nTiles + tile];  // the tensor's amax
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if constexpr (MODE != GIVEN) amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if constexpr (MODE == AMAX) {
+    if (tid == 0) x_scale[(size_t)bh * nTiles + tile] = amax;
+    return;
+  }
 
   // value / scale = z * 448 / amax(z): the rotation's 1/sqrt(d) cancels here
   const bool live = amax >= kMinAmax;
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
 // LDS as one R-byte word, in 16-byte chunks of a column row whose order is
 // XOR-swizzled by the column group (the column groups of a wavefront would
 // otherwise write the same banks).
-template <int D>
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void quant_transpose_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ x8, float* __restrict__ x_scale, int N, int nTiles) {
   constexpr int CG = D / 8;                      // column groups
@@ -223,8 +236,13 @@ __global__ __launch_bounds__(kThreads) void quant_transpose_kernel(
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((tid & 63) == 0) red[tid >> 6] = amax;
+  if constexpr (MODE == GIVEN) amax = x_scale[(size_t)bh * nTiles + tile];  // the tensor's amax
   __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if constexpr (MODE != GIVEN) amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if constexpr (MODE == AMAX) {
+    if (tid == 0) x_scale[(size_t)bh * nTiles + tile] = amax;
+    return;
+  }
   const bool live = amax >= kMinAmax;
   const float mult = live ? 448.0f / amax : 1.0f;
   if (tid == 0) x_scale[(size_t)bh * nTiles + tile] = live ? amax / 448.0f : 1.0f;
@@ -256,22 +274,48 @@ __global__ __launch_bounds__(kThreads) void quant_transpose_kernel(
   }
 }
 
+// The largest of the n amaxes in x_scale, written back into every entry (one
+// workgroup; every read completes before the first write).
+__global__ __launch_bounds__(kThreads) void reduce_amax_kernel(float* __restrict__ x_scale, int n) {
+  __shared__ float red[kThreads / 64];
+  const int tid = threadIdx.x;
+  float amax = 0.f;
+  for (int i = tid; i < n; i += kThreads) amax = fmaxf(amax, x_scale[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  for (int i = tid; i < n; i += kThreads) x_scale[i] = amax;
+}
+
+template <int D, int MODE>
+void launch_mode(const QuantArgs& a, int N, int nTiles, dim3 grid, dim3 block) {
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  if (a.signs) {
+    if (a.transpose_out)
+      hipLaunchKernelGGL((quant_rotate_kernel<D, true, true, MODE>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
+    else
+      hipLaunchKernelGGL((quant_rotate_kernel<D, true, false, MODE>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
+  } else {
+    if (a.transpose_out)
+      hipLaunchKernelGGL((quant_transpose_kernel<D, MODE>), grid, block, 0, a.stream, x, a.x8, a.x_scale, N, nTiles);
+    else
+      hipLaunchKernelGGL((quant_rotate_kernel<D, false, false, MODE>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
+  }
+}
+
 template <int D>
 hipError_t launch_d(const QuantArgs& a) {
   const int BH = (int)(a.B * a.H), N = (int)a.N;
   const int nTiles = (N + kTileRows - 1) / kTileRows;
   const dim3 grid((unsigned)(BH * nTiles)), block(kThreads);
-  const uint16_t* x = static_cast<const uint16_t*>(a.x);
-  if (a.signs) {
-    if (a.transpose_out)
-      hipLaunchKernelGGL((quant_rotate_kernel<D, true, true>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
-    else
-      hipLaunchKernelGGL((quant_rotate_kernel<D, true, false>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
+  if (!a.per_tensor) {
+    launch_mode<D, PER_TILE>(a, N, nTiles, grid, block);
   } else {
-    if (a.transpose_out)
-      hipLaunchKernelGGL((quant_transpose_kernel<D>), grid, block, 0, a.stream, x, a.x8, a.x_scale, N, nTiles);
-    else
-      hipLaunchKernelGGL((quant_rotate_kernel<D, false, false>), grid, block, 0, a.stream, x, a.x8, a.x_scale, a.signs, N, nTiles);
+    launch_mode<D, AMAX>(a, N, nTiles, grid, block);
+    hipLaunchKernelGGL(reduce_amax_kernel, dim3(1), block, 0, a.stream, a.x_scale, BH * nTiles);
+    launch_mode<D, GIVEN>(a, N, nTiles, grid, block);
   }
   return hipGetLastError();
 }

@@ -129,6 +129,22 @@ int fa_quant_rotate_fp8(const void* x, uint8_t* x8, float* x_scale, const int8_t
                         void* stream);
 
 /*
+ * fa_quant_rotate_fp8_tensor -- fa_quant_rotate_fp8 with ONE scale for the whole
+ * tensor instead of one per 128-row tile: the baseline against which the
+ * pages' block quantisation (independent scales of small tiles; page
+ * "FlashAttention-Skalierung, Multi-GPU-Training und Gewichtsquantisierung",
+ * section 1, FlashAttention-3 FP8 item) is measured.  The scale is the largest
+ * magnitude over all B, H, N, d (after the rotation) / 448 -- 1 if that is
+ * below 2^-96 as above -- and is written into every entry of x_scale, so the
+ * output goes to fa_fwd_fp8 unchanged.  Three launches (tile maxima, their
+ * maximum, the quantisation).
+ *   Arguments, layouts and errors: as fa_quant_rotate_fp8.
+ */
+int fa_quant_rotate_fp8_tensor(const void* x, uint8_t* x8, float* x_scale, const int8_t* signs,
+                               int64_t B, int64_t H, int64_t N, int64_t d, int transpose_out,
+                               void* stream);
+
+/*
  * fa_fwd_fp8 -- attention forward on e4m3 operands with per-tile scales: the
  * FP8 variant of the pages (page "FlashAttention-Skalierung, Multi-GPU-
  * Training und Gewichtsquantisierung", section 1, FlashAttention-3 FP8 item:
@@ -158,6 +174,21 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                const float* q_scale, const float* k_scale, const float* v_scale,
                int v_transposed, void* o, float* lse, int64_t B, int64_t H, int64_t N,
                int64_t d, int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_fp8_pbf16 -- fa_fwd_fp8 with the probabilities kept in bf16: the same
+ * fp8 operands, scales and Q K^T product, but P is rounded to bf16 (not e4m3)
+ * and P V runs on the bf16 matrix core with V's codes widened exactly to
+ * bf16.  It isolates the effect of rounding P to FP8 for the accuracy study of
+ * the pages' FP8 item (page "FlashAttention-Skalierung, Multi-GPU-Training und
+ * Gewichtsquantisierung", section 1, FlashAttention-3 FP8 item: FP8 precision
+ * losses and the measures against them); it is not tuned for speed.
+ *   Arguments, layouts and errors: as fa_fwd_fp8.
+ */
+int fa_fwd_fp8_pbf16(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                     const float* q_scale, const float* k_scale, const float* v_scale,
+                     int v_transposed, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+                     int64_t d, int causal, float scale, void* stream);
 
 /*
  * fa_fwd_partial -- attention of queries against one range of keys: the

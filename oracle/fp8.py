@@ -139,6 +139,27 @@ def quantize_rotate(x, signs, tile: int = TILE_ROWS):
     return quantize_tiles(y, tile, bound)
 
 
+def quantize_tensor(y, tile: int = TILE_ROWS, min_amax: float = MIN_AMAX):
+    """e4m3 quantisation of the whole tensor y ([B, H, N, d]) with ONE scale: the
+    baseline of the block quantisation.  scale = amax over every entry / 448 (1 when
+    amax < min_amax); returned like quantize_tiles, the scale repeated in every
+    (b, h, tile) entry so that dequantize and the mirrored oracle apply unchanged."""
+    y = np.asarray(y, dtype=np.float64)
+    B, H, N, d = y.shape
+    amax = float(np.abs(y).max()) if y.size else 0.0
+    sc = amax / E4M3_MAX if amax >= min_amax else 1.0
+    t = y / sc
+    return e4m3_encode(t), np.full((B, H, -(-N // tile)), sc), t
+
+
+def quantize_rotate_tensor(x, signs, tile: int = TILE_ROWS):
+    """Rotate (when signs is not None) then quantise with one scale for the tensor;
+    the zero bound applies as in quantize_rotate."""
+    y = rotate(x, signs)
+    bound = MIN_AMAX if signs is None else MIN_AMAX / np.sqrt(y.shape[-1])
+    return quantize_tensor(y, tile, bound)
+
+
 def dequantize(codes, scales, tile: int = TILE_ROWS) -> np.ndarray:
     """code value x tile scale, float64 [B, H, N, d]."""
     vals = e4m3_decode(codes)

@@ -29,8 +29,8 @@ def fa():
 
 def test_header_declares_the_api():
     assert _declared_functions() == ["fa_abi_version", "fa_bwd", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_fp8",
-                                     "fa_fwd_partial", "fa_fwd_split", "fa_merge", "fa_quant_rotate_fp8",
-                                     "fa_status_string"]
+                                     "fa_fwd_fp8_pbf16", "fa_fwd_partial", "fa_fwd_split", "fa_merge",
+                                     "fa_quant_rotate_fp8", "fa_quant_rotate_fp8_tensor", "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -82,10 +82,10 @@ def test_fwd_validation(fa):
     assert _fwd(fa, q=None, k=None, v=None, o=None, lse=None, B=0) == fa.FA_OK
 
 
-def test_quant_validation(fa):
-    lib = fa.load_library()
-    f = lambda x=P, x8=P2, s=P3, sg=None, B=1, H=1, N=128, d=128, t=0: lib.fa_quant_rotate_fp8(
-        x, x8, s, sg, B, H, N, d, t, None)
+@pytest.mark.parametrize("entry", ["fa_quant_rotate_fp8", "fa_quant_rotate_fp8_tensor"])
+def test_quant_validation(fa, entry):
+    fn = getattr(fa.load_library(), entry)
+    f = lambda x=P, x8=P2, s=P3, sg=None, B=1, H=1, N=128, d=128, t=0: fn(x, x8, s, sg, B, H, N, d, t, None)
     assert f(d=32) == fa.FA_ERR_UNSUPPORTED
     assert f(t=2) == fa.FA_ERR_UNSUPPORTED
     assert f(x=None) == fa.FA_ERR_NULL
@@ -94,9 +94,10 @@ def test_quant_validation(fa):
     assert f(x=None, x8=None, s=None, N=0) == fa.FA_OK
 
 
-def test_fp8_validation(fa):
-    lib = fa.load_library()
-    f = lambda vt=1, d=128, causal=0, scale=0.1, q=P, o=P4: lib.fa_fwd_fp8(
+@pytest.mark.parametrize("entry", ["fa_fwd_fp8", "fa_fwd_fp8_pbf16"])
+def test_fp8_validation(fa, entry):
+    fn = getattr(fa.load_library(), entry)
+    f = lambda vt=1, d=128, causal=0, scale=0.1, q=P, o=P4: fn(
         q, P2, P3, ctypes.c_void_p(0x50000000), ctypes.c_void_p(0x50001000), ctypes.c_void_p(0x50002000), vt,
         o, P5, 1, 1, 256, d, causal, scale, None)
     assert f(vt=0) == fa.FA_ERR_UNSUPPORTED

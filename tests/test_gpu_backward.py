@@ -128,5 +128,22 @@ def test_backward_full_size_heads(fa):
         e = _errors([x[sl] for x in got], ref)
         G.log(f"  head ({b},{h}) normwise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
         assert max(e) <= TOL
-    again = _grads(fa, q, k, v, do, w.causal, w.scale)
-    assert all(torch.equal(x, y) for x, y in zip(got, again))  # no atomics: bitwise reproducible
+    for _ in range(2):  # no atomics: bitwise reproducible
+        again = _grads(fa, q, k, v, do, w.causal, w.scale)
+        assert all(torch.equal(x, y) for x, y in zip(got, again))
+
+
+def test_backward_long_sequence_head(fa):
+    """The long-sequence workload (B1 H32 N16384 d128 causal) in its launch configuration;
+    one whole head against the fp64 gradient oracle (every N x N product materialised)."""
+    w = synthetic.workload("bf16_causal_b1h32n16384d128")
+    G.log(f"case backward {w.name}")
+    q, k, v, _ = synthetic.workload_inputs(w)
+    do = synthetic.draw_qkv(w.B, w.H, w.N, w.d, seed=w.seed + 100, dtype="bf16")[0]
+    got, o = _grads(fa, q, k, v, do, w.causal, w.scale, with_o=True)
+    b, h = 0, 21
+    sl = (slice(b, b + 1), slice(h, h + 1))
+    ref = A.backward(q[sl], k[sl], v[sl], do[sl], w.causal, w.scale, o=o[sl])
+    e = _errors([x[sl] for x in got], ref)
+    G.log(f"  head ({b},{h}) normwise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
+    assert max(e) <= TOL

@@ -130,36 +130,45 @@ def test_workload_full_size(fa, wi):
         eo, el = G.compare_attention(o, lse, q, k, v, w.causal, w.scale, w.dtype, heads=_heads(w.B, w.H, 6))
         G.log(f"  whole heads: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
         assert eo <= tol_o and el <= tol_l
+    else:  # N = 16384: two whole heads, every row against every key (the oracle in row chunks)
+        eo, el = G.compare_attention(o, lse, q, k, v, w.causal, w.scale, w.dtype, heads=[(0, 0), (0, w.H - 1)])
+        G.log(f"  whole heads (0,0), (0,{w.H - 1}): max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+        assert eo <= tol_o and el <= tol_l
     rows = G.sample_rows(w.N, 96, seed=wi)
     eo, el = G.compare_attention(o, lse, q, k, v, w.causal, w.scale, w.dtype,
                                  heads=_heads(w.B, w.H, 16 if w.N > 2048 else 64), rows=rows)
     G.log(f"  sampled rows: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
     assert eo <= tol_o and el <= tol_l
-    # deterministic: a second launch reproduces every bit
-    o2, lse2 = _run(fa, q, k, v, w.causal, w.scale)
-    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    # deterministic: two more launches reproduce every bit
+    for _ in range(2):
+        o2, lse2 = _run(fa, q, k, v, w.causal, w.scale)
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
 # --------------------------------------------------------------------------- fp8
-def _fp8_case(fa, q, k, v, signs, causal, scale):
+def _fp8_case(fa, q, k, v, signs, causal, scale, p_bf16=False, per_tensor=False):
     sg = None if signs is None else torch.from_numpy(signs).to(DEV)
-    o, lse, aux = fa.fp8_attention(q.to(DEV), k.to(DEV), v.to(DEV), sg, causal=causal, scale=scale)
+    o, lse, aux = fa.fp8_attention(q.to(DEV), k.to(DEV), v.to(DEV), sg, causal=causal, scale=scale, p_bf16=p_bf16,
+                                   per_tensor=per_tensor)
     torch.cuda.synchronize()
     return o, lse, aux
 
 
+@pytest.mark.parametrize("per_tensor", [False, True])
 @pytest.mark.parametrize("N", [1, 100, 128, 200, 256, 640])
 @pytest.mark.parametrize("d", [64, 128])
-def test_quantizer_small(fa, N, d):
-    G.log(f"case quantizer N={N} d={d}")
+def test_quantizer_small(fa, N, d, per_tensor):
+    G.log(f"case quantizer N={N} d={d} per_tensor={per_tensor}")
     q, _, _ = synthetic.draw_qkv(2, 2, N, d, seed=N + d, dtype="bf16", outlier_rate=0.01, outlier_scale=50.0)
     signs = synthetic.draw_signs(d, N)
     sg = torch.from_numpy(signs).to(DEV)
     for rot in (True, False):
         for tr in (False, True):
-            x8, xs = fa.fa_quant_rotate_fp8(q.to(DEV), sg if rot else None, tr)
+            x8, xs = fa.fa_quant_rotate_fp8(q.to(DEV), sg if rot else None, tr, per_tensor=per_tensor)
             torch.cuda.synchronize()
-            nb, nt = G.check_codes(x8, xs, q, signs if rot else None, transposed=tr)
+            if per_tensor:
+                assert bool((xs == xs.flatten()[0]).all())  # one scale in every tile entry
+            nb, nt = G.check_codes(x8, xs, q, signs if rot else None, transposed=tr, per_tensor=per_tensor)
             G.log(f"  rotate={rot} transposed={tr}: {nb} of {nt} codes at rounding ties")
             assert nb <= 1e-2 * nt
 
@@ -189,35 +198,43 @@ def test_quantizer_tiny_tile(fa, d, rot):
         assert nb <= 1e-2 * nt
 
 
+@pytest.mark.parametrize("p_bf16", [False, True])
 @pytest.mark.parametrize("outliers", [False, True])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 100, 128, 200, 256, 640])
-def test_fp8_small(fa, N, causal, outliers):
-    G.log(f"case fp8 N={N} causal={causal} outliers={outliers}")
+def test_fp8_small(fa, N, causal, outliers, p_bf16):
+    """G5b on every output; the P-in-bf16 variant rounds P to bf16, so it is held to the
+    bf16 budget (2e-2) in the same scaled metric."""
+    G.log(f"case fp8 N={N} causal={causal} outliers={outliers} p_bf16={p_bf16}")
     d = 128
     q, k, v = synthetic.draw_qkv(1, 2, N, d, seed=3 * N + causal, dtype="bf16",
                                  outlier_rate=1e-3 if outliers else 0.0, outlier_scale=50.0)
     signs = synthetic.draw_signs(d, N + 1)
-    o, lse, (q8, k8, v8t, qs, ks, vs) = _fp8_case(fa, q, k, v, signs, causal, d ** -0.5)
+    o, lse, (q8, k8, v8t, qs, ks, vs) = _fp8_case(fa, q, k, v, signs, causal, d ** -0.5, p_bf16=p_bf16)
     rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, causal, d ** -0.5, heads=[(0, 0), (0, 1)])
     G.log(f"  vs dequantised oracle: scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
-    assert rel <= G.FP8_O_TOL and el <= G.FP8_LSE_TOL
+    assert rel <= (G.FP8_PBF16_O_TOL if p_bf16 else G.FP8_O_TOL) and el <= G.FP8_LSE_TOL
 
 
+@pytest.mark.parametrize("p_bf16", [False, True])
 @pytest.mark.parametrize("scale", [0.0, -0.15, 0.5])
-def test_fp8_scales(fa, scale):
+def test_fp8_scales(fa, scale, p_bf16):
     """Negative scale (every Q code's sign bit flipped), zero scale (Q zeroed), large scale."""
-    G.log(f"case fp8 scale={scale}")
+    G.log(f"case fp8 scale={scale} p_bf16={p_bf16}")
     d, N = 128, 300
     q, k, v = synthetic.draw_qkv(1, 2, N, d, seed=41, dtype="bf16")
     signs = synthetic.draw_signs(d, 42)
-    o, lse, (q8, k8, v8t, qs, ks, vs) = _fp8_case(fa, q, k, v, signs, True, scale)
+    o, lse, (q8, k8, v8t, qs, ks, vs) = _fp8_case(fa, q, k, v, signs, True, scale, p_bf16=p_bf16)
     rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, True, scale, heads=[(0, 0), (0, 1)])
     G.log(f"  vs dequantised oracle: scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
-    assert rel <= G.FP8_O_TOL and el <= G.FP8_LSE_TOL
+    assert rel <= (G.FP8_PBF16_O_TOL if p_bf16 else G.FP8_O_TOL) and el <= G.FP8_LSE_TOL
 
 
 def test_fp8_workload_full_size(fa):
+    """The fp8 workload (B2 H16 N8192, x50 outliers) in the bench's launch configuration.
+    G5a on three whole heads; G5b on two whole heads (all 8192 rows) and sampled rows of a
+    third; the whole-tensor error against the un-quantised inputs gated per head; the
+    P-in-bf16 variant on the same operands; three launches bitwise equal."""
     w = synthetic.WORKLOADS[4]
     G.log(f"case workload {w.name}")
     q, k, v, signs = synthetic.workload_inputs(w)
@@ -230,13 +247,26 @@ def test_fp8_workload_full_size(fa):
             nb, nt = G.check_codes(x8[sl], xs[sl], x[sl], sg, tr)
             G.log(f"  head {(b, h)}: {nb} of {nt} codes at rounding ties")
             assert nb <= 1e-2 * nt
-    # G5b: the attention kernel against the oracle of its dequantised operands
-    rows = G.sample_rows(w.N, 128, seed=4)
-    rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, w.causal, w.scale, heads=heads, rows=rows)
-    G.log(f"  vs dequantised oracle: scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
+    # G5b: the attention kernel against the oracle of its dequantised operands, whole heads
+    rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, w.causal, w.scale, heads=heads[:2])
+    G.log(f"  whole heads {heads[:2]} vs dequantised oracle: scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
     assert rel <= G.FP8_O_TOL and el <= G.FP8_LSE_TOL
-    # reported, not gated: error against the un-quantised inputs (exact oracle)
-    eo, elx = G.compare_attention(o, lse, q, k, v, w.causal, w.scale, "bf16", heads=heads[:1], rows=rows)
-    G.log(f"  vs un-quantised oracle (report only): max|dO| {eo:.3e}  max|dLSE| {elx:.3e}")
-    o2, lse2, _ = _fp8_case(fa, q, k, v, signs, w.causal, w.scale)
-    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    rows = G.sample_rows(w.N, 128, seed=4)
+    rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, w.causal, w.scale, heads=heads[2:], rows=rows)
+    G.log(f"  sampled rows of {heads[2:]}: scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
+    assert rel <= G.FP8_O_TOL and el <= G.FP8_LSE_TOL
+    # against the un-quantised inputs: the method's own error (fp64 attention of the oracle's
+    # quantised operands) is 0.095-0.111 in relative Frobenius norm on these heads; the
+    # device path may add little to it
+    fro = G.rel_frobenius(o, q, k, v, w.causal, w.scale, heads)
+    G.log(f"  vs un-quantised oracle: relative Frobenius error per head {['%.4f' % x for x in fro]}")
+    assert max(fro) <= G.FP8_REL_FRO_BUDGET
+    # the P-in-bf16 variant on the same operands, against the same dequantised oracle
+    o16, l16 = fa.fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal=w.causal, scale=w.scale, p_bf16=True)
+    torch.cuda.synchronize()
+    rel16, ab16, el16 = G.fp8_errors(o16, l16, q8, k8, v8t, qs, ks, vs, w.causal, w.scale, heads=heads[:1])
+    G.log(f"  P in bf16, whole head {heads[0]}: scaled err {rel16:.3e} (abs {ab16:.3e})  LSE rel {el16:.3e}")
+    assert rel16 <= G.FP8_PBF16_O_TOL and el16 <= G.FP8_LSE_TOL
+    for _ in range(2):
+        o2, lse2, _ = _fp8_case(fa, q, k, v, signs, w.causal, w.scale)
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)

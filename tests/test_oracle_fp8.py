@@ -153,6 +153,35 @@ def test_tiny_tile_counts_as_zero():
     assert sc[0, 0, 0] == pytest.approx(2.0 ** -95 / np.sqrt(8) / 448, rel=1e-12)
 
 
+def test_tensor_scale():
+    """One scale for the whole tensor: amax over every (b, h, row, column) / 448, in every
+    tile entry; the amax element maps to 448; one tile of one head is the tile rule; the
+    dequantisation error obeys the same bounds as the tile quantiser, against that scale."""
+    rng = np.random.Generator(np.random.PCG64(29))
+    y = rng.standard_normal((2, 3, 300, 16)) * np.exp(rng.standard_normal((2, 3, 300, 16)))
+    y[1, 2, 77, 5] = -400.0  # the tensor's amax
+    codes, scales, t = F.quantize_tensor(y)
+    assert np.abs(y).max() == 400.0
+    assert scales.shape == (2, 3, 3) and np.all(scales == 400.0 / 448)
+    assert codes[1, 2, 77, 5] == 0xFE  # -448
+    assert np.count_nonzero((codes & 0x7F) == 0x7E) == 1
+    deq = F.dequantize(codes, scales)
+    err = np.abs(deq - y)
+    normal = np.abs(y) >= 2.0 ** -6 * (400.0 / 448)
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(y)[normal] * (1 + 1e-12))
+    assert np.all(err[~normal] <= 2.0 ** -10 * (400.0 / 448) * (1 + 1e-12))
+    one = y[:1, :1, :128]
+    c1, s1, _ = F.quantize_tensor(one)
+    c2, s2, _ = F.quantize_tiles(one)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    # rotated: the same rotation as the tile quantiser, one scale over the rotated tensor
+    s = (rng.integers(0, 2, 16) * 2 - 1).astype(np.int8)
+    c3, s3, _ = F.quantize_rotate_tensor(y, s)
+    c4, s4, _ = F.quantize_tensor(y @ F.rotation_matrix(s))
+    assert np.array_equal(c3, c4) and np.array_equal(s3, s4)
+    assert np.all(F.quantize_tensor(np.zeros((1, 1, 5, 4)))[1] == 1.0)
+
+
 def test_mirrored_oracle_is_exact_on_representable_inputs():
     """Inputs that are e4m3 values times a tile scale quantise losslessly,
     so the mirrored oracle must equal the exact one there."""

@@ -3,8 +3,8 @@
 One step = one pass of the hot path over one batch of synthetic input:
   * bf16 / fp32 workloads: one fa_fwd launch (query blocks x heads grid,
     K/V tiles through LDS, online softmax, epilogue);
-  * the fp8 workload: three quantise+rotate launches (Q, K, V) and one
-    fa_fwd_fp8 launch.
+  * the fp8 workload: one quantise+rotate launch for Q, K and V
+    (fa_quant_rotate_fp8_qkv) and one fa_fwd_fp8 launch.
 Inputs are resident in HBM before the timed region.  FLOPs counted:
 4*B*H*N^2*d, halved when causal (masking waste and exps are not counted).
 
@@ -161,10 +161,8 @@ def make_step(fa, w, dev):
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
-    def prepass():
-        fa.fa_quant_rotate_fp8(q, sg, False, x8=q8, x_scale=qs)
-        fa.fa_quant_rotate_fp8(k, sg, False, x8=k8, x_scale=ks)
-        fa.fa_quant_rotate_fp8(v, None, True, x8=v8t, x_scale=vs)
+    def prepass():  # Q, K rotated, V transposed: one launch
+        fa.fa_quant_rotate_fp8_qkv(q, k, v, sg, out=(q8, k8, v8t, qs, ks, vs))
 
     def attn():
         fa.fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal=w.causal, scale=w.scale, o=o, lse=lse)

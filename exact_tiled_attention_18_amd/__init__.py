@@ -54,6 +54,8 @@ def load_library():
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_quant_rotate_fp8.restype = i32
     lib.fa_quant_rotate_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.fa_quant_rotate_fp8_qkv.restype = i32
+    lib.fa_quant_rotate_fp8_qkv.argtypes = [vp] * 10 + [i64, i64, i64, i64, vp]
     lib.fa_quant_rotate_fp8_tensor.restype = i32
     lib.fa_quant_rotate_fp8_tensor.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
     lib.fa_fwd_fp8.restype = i32
@@ -152,6 +154,33 @@ def fa_quant_rotate_fp8(x, signs=None, transpose_out: bool = False, x8=None, x_s
     return x8, x_scale
 
 
+def fa_quant_rotate_fp8_qkv(q, k, v, signs=None, out=None, stream=None):
+    """The FP8 pre-pass of q, k, v (bfloat16 [B, H, N, d]) in one launch: returns
+    (q8, k8, v8t, q_scale, k_scale, v_scale) as three fa_quant_rotate_fp8 calls would
+    (Q and K with signs, V transposed); `out` may supply those six buffers."""
+    B, H, N, d = q.shape
+    nt = (N + TILE_ROWS - 1) // TILE_ROWS
+    if out is None:
+        q8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=q.device)
+        out = (q8, torch.empty_like(q8), torch.empty((B, H, d, vt_cols(N)), dtype=torch.uint8, device=q.device),
+               *(torch.empty((B, H, nt), dtype=torch.float32, device=q.device) for _ in range(3)))
+    q8, k8, v8t, qs, ks, vs = out
+    _check_dense(q, k, v, signs, *out)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, (B, H, N, d), torch.bfloat16, name)
+    _expect(q8, (B, H, N, d), torch.uint8, "q8")
+    _expect(k8, (B, H, N, d), torch.uint8, "k8")
+    _expect(v8t, (B, H, d, vt_cols(N)), torch.uint8, "v8t")
+    for t, name in ((qs, "q_scale"), (ks, "k_scale"), (vs, "v_scale")):
+        _expect(t, (B, H, nt), torch.float32, name)
+    if signs is not None:
+        _expect(signs, (d,), torch.int8, "signs")
+    lib = load_library()
+    _check(lib.fa_quant_rotate_fp8_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8t), _ptr(qs), _ptr(ks),
+                                       _ptr(vs), _ptr(signs), B, H, N, d, _stream(stream)))
+    return out
+
+
 def fa_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
                o=None, lse=None, stream=None, p_bf16: bool = False):
     """O (bfloat16), LSE from e4m3 Q, K ([B, H, N, d]) and transposed V ([B, H, d, vt_cols(N)]);
@@ -181,13 +210,17 @@ def fa_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, causal: bool = False, sca
 
 def fp8_attention(q, k, v, signs, causal: bool = False, scale: float | None = None, stream=None,
                   per_tensor: bool = False, p_bf16: bool = False):
-    """The FP8 path end to end: three pre-pass calls (Q and K rotated with the
-    same signs, V not rotated and written transposed) and the fp8 forward.
-    per_tensor and p_bf16 select the ablation variants (one scale per tensor;
-    probabilities in bf16).  Returns (o, lse, (q8, k8, v8t, q_scale, k_scale, v_scale))."""
-    q8, qs = fa_quant_rotate_fp8(q, signs, False, stream=stream, per_tensor=per_tensor)
-    k8, ks = fa_quant_rotate_fp8(k, signs, False, stream=stream, per_tensor=per_tensor)
-    v8t, vs = fa_quant_rotate_fp8(v, None, True, stream=stream, per_tensor=per_tensor)
+    """The FP8 path end to end: the pre-pass (Q and K rotated with the same signs, V
+    not rotated and written transposed; one fused launch) and the fp8 forward.
+    per_tensor and p_bf16 select the ablation variants (one scale per tensor, three
+    pre-pass calls; probabilities in bf16).  Returns (o, lse, (q8, k8, v8t, q_scale,
+    k_scale, v_scale))."""
+    if per_tensor:
+        q8, qs = fa_quant_rotate_fp8(q, signs, False, stream=stream, per_tensor=True)
+        k8, ks = fa_quant_rotate_fp8(k, signs, False, stream=stream, per_tensor=True)
+        v8t, vs = fa_quant_rotate_fp8(v, None, True, stream=stream, per_tensor=True)
+    else:
+        q8, k8, v8t, qs, ks, vs = fa_quant_rotate_fp8_qkv(q, k, v, signs, stream=stream)
     o, lse = fa_fwd_fp8(q8, k8, v8t, qs, ks, vs, causal, scale, stream=stream, p_bf16=p_bf16)
     return o, lse, (q8, k8, v8t, qs, ks, vs)
 

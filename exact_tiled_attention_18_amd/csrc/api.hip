@@ -139,6 +139,37 @@ int fa_quant_rotate_fp8_tensor(const void* x, uint8_t* x8, float* x_scale, const
   return quant_rotate(x, x8, x_scale, signs, B, H, N, d, transpose_out, stream, 1);
 }
 
+int fa_quant_rotate_fp8_qkv(const void* q, const void* k, const void* v, uint8_t* q8, uint8_t* k8, uint8_t* v8t,
+                            float* q_scale, float* k_scale, float* v_scale, const int8_t* signs, int64_t B,
+                            int64_t H, int64_t N, int64_t d, void* stream) {
+  int64_t n = 0;
+  if (int st = shape_status(B, H, N, d, &n)) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (n == 0) return FA_OK;
+  const void* in[3] = {q, k, v};
+  uint8_t* out[3] = {q8, k8, v8t};
+  float* sc[3] = {q_scale, k_scale, v_scale};
+  for (int i = 0; i < 3; ++i) {
+    if (!in[i] || !out[i] || !sc[i]) return FA_ERR_NULL;
+    if (!aligned(in[i], 16) || !aligned(out[i], 16) || !aligned(sc[i], 4)) return FA_ERR_UNSUPPORTED;
+  }
+  const int64_t sb = B * H * ((N + 127) / 128) * 4;
+  const int64_t ob[3] = {n, n, B * H * d * FA_FP8_VT_COLS(N)};
+  // no output may overlap an input, the signs or another output
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(out[i], ob[i], in[j], 2 * n) || overlaps(sc[i], sb, in[j], 2 * n)) return FA_ERR_ALIAS;
+    if (signs && (overlaps(out[i], ob[i], signs, d) || overlaps(sc[i], sb, signs, d))) return FA_ERR_ALIAS;
+    for (int j = 0; j < 3; ++j) {
+      if (overlaps(out[i], ob[i], sc[j], sb)) return FA_ERR_ALIAS;
+      if (j != i && (overlaps(out[i], ob[i], out[j], ob[j]) || overlaps(sc[i], sb, sc[j], sb))) return FA_ERR_ALIAS;
+    }
+  }
+  const fa::QkvQuantArgs a{{q, k, v}, {q8, k8, v8t}, {q_scale, k_scale, v_scale}, signs, B, H, N, d,
+                           static_cast<hipStream_t>(stream)};
+  return hip_status(fa::launch_quant_qkv_fp8(a));
+}
+
 }  // extern "C"
 
 namespace {

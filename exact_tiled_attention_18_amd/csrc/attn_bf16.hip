@@ -553,6 +553,10 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
   s.load_tile(s.vrs, 1, s.stg_v);
   s.kop[0] = s.read_k(1, 0);
   s.vop[0] = s.read_v(2, 0);
+  // step 0 stores K_3 into slot 0, so every wavefront must have read K_0 for S_0 first
+  // (in practice its reads finish long before the K_3 load returns; the barrier makes
+  // the order certain)
+  __syncthreads();
 
   // ---- steps; the slot of tile j is j % 3
   int sk_next = 1, sk_w = 0, sv_pv = 2, sv_next = 0, sv_w = 1;  // for t = 0

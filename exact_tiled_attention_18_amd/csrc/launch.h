@@ -77,6 +77,17 @@ struct QuantArgs {
 };
 hipError_t launch_quant_rotate_fp8(const QuantArgs& a);
 
+// Q and K (rotated when signs is set) and V (transposed codes) in one launch.
+struct QkvQuantArgs {
+  const void* x[3];   // q, k, v
+  uint8_t* x8[3];     // q8, k8 ([B, H, N, d]), v8t ([B, H, d, N64])
+  float* scale[3];
+  const int8_t* signs;
+  int64_t B, H, N, d;
+  hipStream_t stream;
+};
+hipError_t launch_quant_qkv_fp8(const QkvQuantArgs& a);
+
 struct Fp8AttnArgs {
   const uint8_t* q8;
   const uint8_t* k8;

@@ -53,21 +53,23 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
-// DPP move: `old` where the control's lane is invalid or the bank is masked off
-template <int CTRL, int BANK>
-__device__ __forceinline__ float dpp(float old, float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, 0xF, BANK, false));
+// DPP move of x over the whole wave (every lane written, so no old value is needed)
+template <int CTRL>
+__device__ __forceinline__ float dpp_all(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 // value held by the lane whose index differs in bit HM (HM = 1, 2, 4, 8; inside 16-lane rows)
 template <int HM>
 __device__ __forceinline__ float partner(float x) {
-  if constexpr (HM == 1) return dpp<0xB1, 0xF>(x, x);  // quad_perm [1, 0, 3, 2]
-  if constexpr (HM == 2) return dpp<0x4E, 0xF>(x, x);  // quad_perm [2, 3, 0, 1]
+  if constexpr (HM == 1) return dpp_all<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+  if constexpr (HM == 2) return dpp_all<0x4E>(x);  // quad_perm [2, 3, 0, 1]
   if constexpr (HM == 4) {
-    const float up = dpp<0x104, 0x5>(x, x);  // row_shl:4 into lanes 0-3 and 8-11 of each row
-    return dpp<0x114, 0xA>(up, x);           // row_shr:4 into lanes 4-7 and 12-15
+    // row_shl:4 into lanes 0-3 and 8-11 of each row (the other lanes are written next),
+    // then row_shr:4 into lanes 4-7 and 12-15
+    const float up = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x104, 0xF, 0x5, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(up), __float_as_int(x), 0x114, 0xF, 0xA, false));
   }
-  return dpp<0x128, 0xF>(x, x);              // row_ror:8
+  return dpp_all<0x128>(x);                          // row_ror:8
 }
 
 template <int HM>
@@ -77,10 +79,12 @@ __device__ __forceinline__ void butterfly(float (&z)[8], int cg) {
   for (int e = 0; e < 8; ++e) z[e] = fmaf(z[e], sgn, partner<HM>(z[e]));
 }
 
+// One 128-row tile (work item `item` = bh * nTiles + tile) of one tensor, row by row:
+// optional sign flip and Hadamard transform, amax, codes row-major or transposed.
 template <int D, bool ROTATE, bool TRANSPOSE, int MODE>
-__global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ x8, float* __restrict__ x_scale,
-    const int8_t* __restrict__ signs, int N, int nTiles) {
+__device__ __forceinline__ void rotate_tile(const uint16_t* __restrict__ x, uint8_t* __restrict__ x8,
+                                            float* __restrict__ x_scale, const int8_t* __restrict__ signs, int N,
+                                            int nTiles, int item) {
   constexpr int TPR = D / 8;                 // threads per row (8 values each)
   static_assert(TPR == 8 || TPR == 16, "row groups of 8 or 16 lanes");
   constexpr int RPP = kThreads / TPR;        // rows per pass
@@ -88,8 +92,8 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
   __shared__ float red[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint8_t tr[TRANSPOSE ? D * (kTileRows + 16) : 1];
 
-  const int tile = blockIdx.x % nTiles;
-  const int bh = blockIdx.x / nTiles;
+  const int tile = item % nTiles;
+  const int bh = item / nTiles;
   const int tid = threadIdx.x;
   const int cg = tid % TPR;  // column group: columns 8*cg .. 8*cg+7
   const int r0 = tile * kTileRows;
@@ -202,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void quant_rotate_kernel(
 // XOR-swizzled by the column group (the column groups of a wavefront would
 // otherwise write the same banks).
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) void quant_transpose_kernel(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ x8, float* __restrict__ x_scale, int N, int nTiles) {
+__device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ x, uint8_t* __restrict__ x8,
+                                               float* __restrict__ x_scale, int N, int nTiles, int item) {
   constexpr int CG = D / 8;                      // column groups
   constexpr int R = kTileRows * CG / kThreads;   // rows per thread
   static_assert(R == 4 || R == 8, "4 or 8 rows per thread");
@@ -211,8 +215,8 @@ __global__ __launch_bounds__(kThreads) void quant_transpose_kernel(
   __shared__ float red[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint8_t tr[D * LD];
 
-  const int tile = blockIdx.x % nTiles;
-  const int bh = blockIdx.x / nTiles;
+  const int tile = item % nTiles;
+  const int bh = item / nTiles;
   const int tid = threadIdx.x;
   const int cg = tid % CG, j = tid / CG;
   const int r0 = tile * kTileRows;
@@ -274,6 +278,39 @@ __global__ __launch_bounds__(kThreads) void quant_transpose_kernel(
   }
 }
 
+template <int D, bool ROTATE, bool TRANSPOSE, int MODE>
+__global__ __launch_bounds__(kThreads) void quant_rotate_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ x8,
+                                                                float* __restrict__ x_scale,
+                                                                const int8_t* __restrict__ signs, int N, int nTiles) {
+  rotate_tile<D, ROTATE, TRANSPOSE, MODE>(x, x8, x_scale, signs, N, nTiles, blockIdx.x);
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kThreads) void quant_transpose_kernel(const uint16_t* __restrict__ x,
+                                                                   uint8_t* __restrict__ x8,
+                                                                   float* __restrict__ x_scale, int N, int nTiles) {
+  transpose_tile<D, MODE>(x, x8, x_scale, N, nTiles, blockIdx.x);
+}
+
+// The whole pre-pass of the FP8 path in one launch: work items [0, T) are Q's tiles,
+// [T, 2T) K's (both rotated when ROTATE), [2T, 3T) V's (codes transposed), T = B*H*nTiles.
+struct QkvPtrs {
+  const uint16_t* x[3];
+  uint8_t* x8[3];
+  float* scale[3];
+};
+template <int D, bool ROTATE>
+__global__ __launch_bounds__(kThreads) void quant_qkv_kernel(QkvPtrs p, const int8_t* __restrict__ signs, int N,
+                                                             int nTiles, int T) {
+  const int item = blockIdx.x;
+  if (item < T)
+    rotate_tile<D, ROTATE, false, PER_TILE>(p.x[0], p.x8[0], p.scale[0], signs, N, nTiles, item);
+  else if (item < 2 * T)
+    rotate_tile<D, ROTATE, false, PER_TILE>(p.x[1], p.x8[1], p.scale[1], signs, N, nTiles, item - T);
+  else
+    transpose_tile<D, PER_TILE>(p.x[2], p.x8[2], p.scale[2], N, nTiles, item - 2 * T);
+}
+
 // The largest of the n amaxes in x_scale, written back into every entry (one
 // workgroup; every read completes before the first write).
 __global__ __launch_bounds__(kThreads) void reduce_amax_kernel(float* __restrict__ x_scale, int n) {
@@ -320,10 +357,33 @@ hipError_t launch_d(const QuantArgs& a) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_qkv_d(const QkvQuantArgs& a) {
+  const int BH = (int)(a.B * a.H), N = (int)a.N;
+  const int nTiles = (N + kTileRows - 1) / kTileRows;
+  const int T = BH * nTiles;
+  QkvPtrs p;
+  for (int i = 0; i < 3; ++i) {
+    p.x[i] = static_cast<const uint16_t*>(a.x[i]);
+    p.x8[i] = a.x8[i];
+    p.scale[i] = a.scale[i];
+  }
+  const dim3 grid((unsigned)(3 * T)), block(kThreads);
+  if (a.signs)
+    hipLaunchKernelGGL((quant_qkv_kernel<D, true>), grid, block, 0, a.stream, p, a.signs, N, nTiles, T);
+  else
+    hipLaunchKernelGGL((quant_qkv_kernel<D, false>), grid, block, 0, a.stream, p, a.signs, N, nTiles, T);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quant_rotate_fp8(const QuantArgs& a) {
   return a.d == 64 ? launch_d<64>(a) : launch_d<128>(a);
+}
+
+hipError_t launch_quant_qkv_fp8(const QkvQuantArgs& a) {
+  return a.d == 64 ? launch_qkv_d<64>(a) : launch_qkv_d<128>(a);
 }
 
 }  // namespace fa

@@ -145,6 +145,24 @@ int fa_quant_rotate_fp8_tensor(const void* x, uint8_t* x8, float* x_scale, const
                                void* stream);
 
 /*
+ * fa_quant_rotate_fp8_qkv -- the whole FP8 pre-pass in one launch: the three
+ * fa_quant_rotate_fp8 calls the FP8 path makes (same page and item as above),
+ * with identical results -- Q and K with `signs` (rotated; NULL: not rotated)
+ * into row-major codes, V without rotation into transposed codes.
+ *   q, k, v : bfloat16 [B, H, N, d].
+ *   q8, k8  : e4m3 codes [B, H, N, d];  v8t: e4m3 codes [B, H, d, FA_FP8_VT_COLS(N)].
+ *   q_scale, k_scale, v_scale : float32 [B, H, ceil(N/128)].
+ *   signs   : int8 [d] of +1/-1 (device) or NULL.   d: 64 or 128.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED (d, alignment),
+ * FA_ERR_ALIAS (an output overlapping an input, the signs or another output),
+ * FA_ERR_HIP.
+ */
+int fa_quant_rotate_fp8_qkv(const void* q, const void* k, const void* v, uint8_t* q8, uint8_t* k8,
+                            uint8_t* v8t, float* q_scale, float* k_scale, float* v_scale,
+                            const int8_t* signs, int64_t B, int64_t H, int64_t N, int64_t d,
+                            void* stream);
+
+/*
  * fa_fwd_fp8 -- attention forward on e4m3 operands with per-tile scales: the
  * FP8 variant of the pages (page "FlashAttention-Skalierung, Multi-GPU-
  * Training und Gewichtsquantisierung", section 1, FlashAttention-3 FP8 item:

@@ -30,7 +30,8 @@ def fa():
 def test_header_declares_the_api():
     assert _declared_functions() == ["fa_abi_version", "fa_bwd", "fa_bwd_noalloc", "fa_fwd", "fa_fwd_fp8",
                                      "fa_fwd_fp8_pbf16", "fa_fwd_partial", "fa_fwd_split", "fa_merge",
-                                     "fa_quant_rotate_fp8", "fa_quant_rotate_fp8_tensor", "fa_status_string"]
+                                     "fa_quant_rotate_fp8", "fa_quant_rotate_fp8_qkv", "fa_quant_rotate_fp8_tensor",
+                                     "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(fa):
@@ -212,4 +213,23 @@ def test_bwd_noalloc_validation(fa):
     assert _bwd_noalloc(fa, scale=float("nan")) == fa.FA_ERR_SCALE
     assert _bwd_noalloc(fa, dv=None) == fa.FA_ERR_NULL
     assert _bwd_noalloc(fa, N=0, **none) == fa.FA_OK
+
+
+def test_quant_qkv_validation(fa):
+    lib = fa.load_library()
+    A = [ctypes.c_void_p(0x10000000 * (i + 1)) for i in range(9)]  # q, k, v, q8, k8, v8t, scales: disjoint
+
+    def f(i=None, val=None, d=128, N=256, sg=None):
+        args = list(A)
+        if i is not None:
+            args[i] = val
+        return lib.fa_quant_rotate_fp8_qkv(*args, sg, 1, 2, N, d, None)
+    assert f(d=32) == fa.FA_ERR_UNSUPPORTED
+    assert f(N=-1) == fa.FA_ERR_SHAPE
+    assert f(0, None) == fa.FA_ERR_NULL and f(8, None) == fa.FA_ERR_NULL
+    assert f(4, ctypes.c_void_p(0x10000000 * 4 + 64)) == fa.FA_ERR_ALIAS   # k8 inside q8
+    assert f(5, ctypes.c_void_p(0x10000000 * 2 + 32)) == fa.FA_ERR_ALIAS   # v8t inside k
+    assert f(7, ctypes.c_void_p(0x10000000 * 7 + 8)) == fa.FA_ERR_ALIAS    # k_scale inside q_scale (16 bytes)
+    assert f(3, ctypes.c_void_p(0x10000000 * 4 + 8)) == fa.FA_ERR_UNSUPPORTED  # misaligned q8
+    assert lib.fa_quant_rotate_fp8_qkv(*([None] * 9), None, 1, 2, 0, 128, None) == fa.FA_OK
 

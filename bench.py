@@ -74,16 +74,50 @@ def algorithmic_bytes(w) -> float:
     return 3 * n + scales + 2 * n + lse
 
 
-def copy_calibration(mib: int, dev) -> None:
-    """A plain device-to-device copy of known size (mib MiB read, mib MiB written),
-    launched a few times so that a counter pass over this program can relate
-    FETCH_SIZE / WRITE_SIZE to bytes actually moved."""
+def copy_calibration(fa, mib: int, dev) -> None:
+    """The library's plain copy kernel over a known size (mib MiB read, mib MiB
+    written), launched a few times so that a counter pass over this program can
+    relate FETCH_SIZE / WRITE_SIZE to bytes actually moved."""
     x = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
     for _ in range(3):
-        y.copy_(x)
+        fa.fa_calib_copy(x, y)
     torch.cuda.synchronize()
     del x, y
+
+
+def calibrate(fa, dev) -> dict:
+    """What the chip sustains in this process for the resources the kernels are priced
+    against: MFMA-only kernels (bf16 and fp8; 3 wavefronts per SIMD, nothing but
+    independent MFMAs), a 1 GiB streaming copy and a 1 GiB streaming read, each timed
+    with HIP events after 0.2 s of warm-up."""
+    def rate(fn, work: float, reps: int) -> float:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
+            fn()
+            torch.cuda.synchronize()
+        return work / time_loop(fn, reps)
+
+    out = {}
+    wgs, iters = 3 * 256, 20000  # three 4-wavefront workgroups per compute unit, all resident
+    for kind in ("bf16", "fp8"):
+        buf = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+        flop = fa.fa_calib_mfma(kind, wgs, iters, out=buf)[1]
+        r = rate(lambda k=kind, b=buf: fa.fa_calib_mfma(k, wgs, iters, out=b), flop, 10) / 1e12
+        out[f"mfma_{kind}"] = {"tflops": round(r, 1), "frac_of_peak": round(r / PEAK_TFLOPS[kind], 4)}
+    x = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    r = rate(lambda: fa.fa_calib_copy(x, y), 2.0 * (1 << 30), 20) / 1e9
+    out["copy"] = {"gbs": round(r, 1), "frac_of_peak": round(r / HBM_GBPS, 4), "bytes": 2 * (1 << 30),
+                   "note": "1 GiB read + 1 GiB written per launch"}
+    del y
+    sink = torch.empty(fa.CALIB_READ_OUT_WORDS, dtype=torch.int32, device=dev)
+    r = rate(lambda: fa.fa_calib_read(x, out=sink), 1.0 * (1 << 30), 20) / 1e9
+    out["read"] = {"gbs": round(r, 1), "frac_of_peak": round(r / HBM_GBPS, 4), "bytes": 1 << 30,
+                   "note": "1 GiB read per launch"}
+    del x, sink
+    eprint("calibration: " + ", ".join(f"{k} {v.get('tflops', v.get('gbs'))}" for k, v in out.items()))
+    return out
 
 
 def _counter_rows(path: str):
@@ -120,13 +154,15 @@ def write_traffic(workload: str, attn_tag: str, src: str, algorithmic: float, fe
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
         rows = _counter_rows(path)
-        # the calibration copies are the runtime's buffer-copy kernel at its largest grid
-        # (other, small copies of the same kernel move the inputs of the run)
-        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        # the calibration copies: the library's copy kernel (older runs: the runtime's
+        # buffer-copy kernel at its largest grid; small copies of that kernel move the
+        # inputs of the run)
+        tag = "copy16_kernel" if any("copy16_kernel" in r["Kernel_Name"] for r in rows) else "copyBuffer"
+        copies = [r for r in rows if tag in r["Kernel_Name"]]
         if not copies:
-            raise SystemExit(f"no buffer-copy dispatches in {path}")
+            raise SystemExit(f"no calibration-copy dispatches in {path}")
         grid = max(int(r["Grid_Size"]) for r in copies)
-        is_copy = lambda r, g=grid: "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) == g  # noqa: E731
+        is_copy = lambda r, g=grid: tag in r["Kernel_Name"] and int(r["Grid_Size"]) == g  # noqa: E731
         kib, n = _mean_counter(rows, counter, is_attn)
         ckib, cn = _mean_counter(rows, counter, is_copy)
         factor = known / (ckib * 1024.0)
@@ -455,6 +491,8 @@ def main():
                     help="time the backward pass (fa_bwd) of a bf16 workload instead of the forward")
     ap.add_argument("--split-kv", action="store_true",
                     help="time a decode-shaped split-KV forward (one fa_fwd_split launch + fa_merge)")
+    ap.add_argument("--no-calibration", dest="calibrate", action="store_false",
+                    help="skip the MFMA-only and copy calibration kernels")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run a plain copy of this many MiB (for counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -485,7 +523,7 @@ def main():
     dev = "cuda:0"
     w = synthetic.workload(args.workload)
     if args.copy_calibration_mib > 0:
-        copy_calibration(args.copy_calibration_mib, dev)
+        copy_calibration(fa, args.copy_calibration_mib, dev)
     if args.split_kv:
         bench_split_kv(fa, dev, args)
         return
@@ -500,7 +538,13 @@ def main():
                 ew = synthetic.workload(name)
                 m = measure_forward(fa, ew, dev, args.steps, args.warmup, args.extra_warmup_s, 0, False)
                 extra[name] = forward_record(ew, m)
+        calib = calibrate(fa, dev) if args.calibrate else None
     r = forward_record(w, main_m)
+    if calib:
+        for rr, ww in [(r, w)] + [(extra[n], synthetic.workload(n)) for n in extra]:
+            sus = calib[f"mfma_{'fp8' if ww.dtype == 'fp8' else 'bf16'}"]["tflops"] if ww.dtype != "f32" else None
+            if sus:
+                rr["roofline"]["frac_of_sustained_mfma"] = round(rr["roofline"]["achieved"] / sus, 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_budget)
     rec = {
         "metric": "attention fwd TFLOP/s at 1 MI355X and % of dense MFMA peak (bf16, fp8)",
@@ -512,6 +556,7 @@ def main():
         "windows": r["windows"], "cold_cache": r["cold_cache"],
         "roofline": r["roofline"], "cpu_baseline": cpu,
         "sclk": sclk.summary(),
+        "calibration": calib,
         "extra": extra or None,
     }
     print(json.dumps(rec), flush=True)

@@ -17,6 +17,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
+# debug build: the bf16 forward's loop in its serial form (one tile at a time, one LDS
+# slot, full barriers); it must agree with libfa.so bit for bit
+SERIAL_LIB_PATH = os.path.join(_HERE, "libfa_serial.so")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_SCALE, FA_ERR_ALIAS, FA_ERR_HIP, FA_ERR_SCRATCH = range(8)
 FA_BWD_NOALLOC_MAX_ROWS = 1 << 22  # rows (B * H * N) of fa_bwd_noalloc's static workspace
@@ -40,11 +43,20 @@ class FAError(RuntimeError):
 def load_library():
     """Load libfa.so (raises if it has not been built)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"HIP library {LIB_PATH} is not built; run __graft_entry__.build() first")
-    lib = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+def load_serial_library():
+    """Load the debug build libfa_serial.so (same C-ABI; raises if it has not been built)."""
+    return _open(SERIAL_LIB_PATH)
+
+
+def _open(path):
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     lib.fa_abi_version.restype = i32
     lib.fa_abi_version.argtypes = []
@@ -72,7 +84,12 @@ def load_library():
     lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i64, i64, i64, i64, i32, f32, i32, vp]
     lib.fa_merge.restype = i32
     lib.fa_merge.argtypes = [vp, vp, i64, vp, vp, i64, i64, i64, i64, i32, vp]
-    _lib = lib
+    lib.fa_calib_mfma.restype = i32
+    lib.fa_calib_mfma.argtypes = [i32, i64, i64, vp, vp]
+    lib.fa_calib_copy.restype = i32
+    lib.fa_calib_copy.argtypes = [vp, vp, i64, vp]
+    lib.fa_calib_read.restype = i32
+    lib.fa_calib_read.argtypes = [vp, i64, vp, vp]
     return lib
 
 
@@ -350,3 +367,43 @@ def fa_bwd_noalloc(q, k, v, o, dout, lse, causal: bool = False, scale: float | N
     _check(lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                               _ptr(dv), B, H, N, d, int(causal), float(scale), FA_BF16, _stream(stream)))
     return dq, dk, dv
+
+
+# ---- calibration kernels (include/fa_calib.h): not part of the method; they measure
+# what the chip sustains for the resources the attention kernels are priced against
+
+CALIB_MFMA_FLOP = {"bf16": 32768, "fp8": 131072}  # per instruction
+
+
+def fa_calib_mfma(kind: str, workgroups: int, iters: int, out=None, stream=None):
+    """Launches the MFMA-only kernel (kind "bf16" or "fp8"); returns (out, FLOP per launch)."""
+    code = {"bf16": 0, "fp8": 1}[kind]
+    if out is None:
+        out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    _expect(out, (workgroups * 256,), torch.float32, "out")
+    _check(load_library().fa_calib_mfma(code, workgroups, iters, _ptr(out), _stream(stream)))
+    return out, workgroups * 4 * iters * 4 * CALIB_MFMA_FLOP[kind]
+
+
+def fa_calib_copy(src, dst, stream=None):
+    """dst[:] = src[:] (contiguous device tensors of the same byte size, a multiple of 16)."""
+    _check_dense(src, dst)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst differ in size")
+    _check(load_library().fa_calib_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+    return dst
+
+
+CALIB_READ_OUT_WORDS = 16384 * 256
+
+
+def fa_calib_read(src, out=None, stream=None):
+    """Reads every byte of src (a contiguous device tensor, size a multiple of 16) once;
+    out (int32 [CALIB_READ_OUT_WORDS]) receives per-thread XORs."""
+    if out is None:
+        out = torch.empty(CALIB_READ_OUT_WORDS, dtype=torch.int32, device=src.device)
+    _check_dense(src, out)
+    _expect(out, (CALIB_READ_OUT_WORDS,), torch.int32, "out")
+    _check(load_library().fa_calib_read(_ptr(src), src.numel() * src.element_size(), _ptr(out), _stream(stream)))
+    return out

@@ -1,8 +1,10 @@
 // C-ABI entry points: argument validation, then one enqueue per kernel.
 // Validation never touches the GPU, so a rejected call has no side effect.
+// Plain host C++: every GPU action goes through the launchers of launch.h, so
+// this file also builds with a host compiler against a recording stand-in for
+// them (the sanitizer build of the validation code).
 #include <cmath>
 #include <cstdint>
-#include <mutex>
 
 #include "fa.h"
 #include "launch.h"
@@ -38,29 +40,6 @@ bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
 bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
-
-// fa_bwd_noalloc's workspace: one static array per GPU (each device holds its own
-// copy, at its own address).  In host code `scratch` names a host-side stand-in,
-// not device memory, so the kernels only ever get the device address looked up
-// below, one per device.
-__device__ __align__(256) float scratch[FA_BWD_NOALLOC_MAX_ROWS];
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void* g_scratch_ptr[kMaxDevices] = {};
-
-// Device address of the current device's `scratch` (looked up once per device).
-int scratch_address(void** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_ptr[dev]) {
-    void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
-    g_scratch_ptr[dev] = p;
-  }
-  *out = g_scratch_ptr[dev];
-  return FA_OK;
-}
 
 }  // namespace
 
@@ -318,7 +297,7 @@ int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, c
   if (n == 0) return FA_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   void* ws = nullptr;
-  if (int st = scratch_address(&ws)) return st;
+  if (fa::scratch_address(&ws) != hipSuccess || !ws) return FA_ERR_HIP;
   // the workspace is library memory, so it overlaps none of the caller's buffers
   return fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(ws), B, H, N, d, causal, scale, dtype,
                 stream);

@@ -69,6 +69,10 @@
 #ifndef FA_BF16_QB
 #define FA_BF16_QB 1
 #endif
+// FA_SERIAL_PIPELINE=1 builds the debug form of the forward loop (see serial_steps)
+#ifndef FA_SERIAL_PIPELINE
+#define FA_SERIAL_PIPELINE 0
+#endif
 
 namespace fa {
 namespace {
@@ -394,6 +398,50 @@ struct Attn {
     load_tile(vrs, t + 2, stg_v);
     __syncthreads();
   }
+
+  // ---- debug form of the loop (FA_SERIAL_PIPELINE builds): one tile at a time
+  // through a single LDS slot, a full barrier on each side of every copy, nothing
+  // overlapped.  Scores, softmax, rescale and products are the same operations in
+  // the same order as in the pipelined steps (the pipeline applies the correction
+  // factor of tile t after adding P_{t-1} V_{t-1}, which is this loop's
+  // "rescale, then add P_t V_t" one tile later), so the two builds agree bit for
+  // bit, and a difference points at a hazard in the pipelined schedule.
+  __device__ void serial_steps(int nT, int last_w) {
+    for (int t = 0; t < nT; ++t) {
+      load_tile(krs, t, stg_k);
+      load_tile(vrs, t, stg_v);
+      __syncthreads();  // every wavefront is done with tile t - 1
+      store_tile(kslot, kst_off, Ly::KS, stg_k);
+      store_tile(vslot, vst_off, Ly::VS, stg_v);
+      __syncthreads();
+      if (t > last_w) continue;  // no row of this wavefront sees tile t (uniform)
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sbuf[0][qb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const bf16x8 a = read_k(0, ks);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) sbuf[0][qb] = mfma(a, qf[qb][ks], sbuf[0][qb]);
+      }
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) softmax_slice<true>(ch, 0, t);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][qb][r] *= alpha[qb];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const bf16x8 a = read_v(0, ch);
+        const int db = ch % DB, mm = ch / DB;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) oacc[db][qb] = mfma(a, pbuf[0][qb][mm], oacc[db][qb]);
+      }
+    }
+  }
 };
 
 // Rows of one launch: queries 0 .. nq-1 of each head against keys k0 .. k0+kn-1 of
@@ -500,9 +548,11 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
   // the first tiles' loads go out together, ahead of the Q loads: each would
   // otherwise wait for its own memory round trip before the next is issued
   uint4 pro_k[3][Ly::CHUNKS], pro_v[Ly::CHUNKS];
+  if constexpr (!FA_SERIAL_PIPELINE) {
 #pragma unroll
-  for (int j = 0; j < 3; ++j) s.load_tile(s.krs, j, pro_k[j]);
-  s.load_tile(s.vrs, 0, pro_v);
+    for (int j = 0; j < 3; ++j) s.load_tile(s.krs, j, pro_k[j]);
+    s.load_tile(s.vrs, 0, pro_v);
+  }
 
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -526,6 +576,18 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
       for (int r = 0; r < 16; ++r) s.oacc[db][qb][r] = 0.f;
   }
 
+  // the wavefront's own last tile: the last one holding a key visible to one of its
+  // rows (wavefront-uniform; tiles up to nFull - 1 are visible to every row); -1 for
+  // a wavefront whose rows all lie past N (a short last block, decode), which then
+  // only helps with the tile copies
+  const auto wave_last_tile = [&]() {
+    const int lw = CAUSAL ? min(gm.qpos + s.qw0 + kW - 1, gm.kn - 1) : gm.kn - 1;
+    return __builtin_amdgcn_readfirstlane(s.qw0 >= N || lw < 0 ? -1 : lw / kBc);
+  };
+
+  if constexpr (FA_SERIAL_PIPELINE) {
+    s.serial_steps(nT, wave_last_tile());
+  } else {
   // ---- prologue: K_0, K_1, K_2 and V_0 into LDS, V slot 2 (standing for V_{-1}) and
   // P_{-1} zero; S_0; stage K_3 and V_1; operands of step 0's first chunk
 #pragma unroll
@@ -569,12 +631,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
   };
   // steps with 1 <= t and tiles t, t+1 unmasked need no mask.  Buffer parity
   // B = t % 2 is static: every loop below starts at an odd t and advances by two.
-  // the wavefront's own last tile: the last one holding a key visible to one of its
-  // rows (wavefront-uniform; tiles up to nFull - 1 are visible to every row); -1 for
-  // a wavefront whose rows all lie past N (a short last block, decode), which then
-  // only helps with the tile copies
-  int last_w = CAUSAL ? min(gm.qpos + s.qw0 + kW - 1, gm.kn - 1) : gm.kn - 1;
-  last_w = __builtin_amdgcn_readfirstlane(s.qw0 >= N || last_w < 0 ? -1 : last_w / kBc);
+  const int last_w = wave_last_tile();
   const int steady_end = min(nFull - 1, last_w + 1);
   s.template step<true, 0>(0, sk_next, sk_w, sv_pv, sv_next, sv_w);
   advance();
@@ -624,6 +681,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 128 ? 2 : 3) void attn_fwd_bf16_ke
     if ((nT - 1) & 1) s.template last_pv<1>((nT - 1) % kSlots);
     else s.template last_pv<0>((nT - 1) % kSlots);
   }
+  }  // pipelined loop
 
   // ---- epilogue: the single division by the row sum, LSE, stores
 #pragma unroll

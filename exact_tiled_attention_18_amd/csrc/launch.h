@@ -1,9 +1,9 @@
 // Host-side launchers, one per kernel family.  Each validates nothing (the
-// C-ABI entry points in api.hip do that) and returns the hipError_t of its
-// launch.
+// C-ABI entry points in api.cpp do that) and returns the hipError_t of its
+// launch.  Only runtime API types appear here, so host C++ can include it.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace fa {
@@ -104,5 +104,9 @@ struct Fp8AttnArgs {
   int p_bf16;  // 1: probabilities in bf16, P V on the bf16 matrix core
 };
 hipError_t launch_attn_fp8(const Fp8AttnArgs& a);
+
+// Device address of fa_bwd_noalloc's static workspace on the current device
+// (FA_BWD_NOALLOC_MAX_ROWS floats; looked up once per device, then cached).
+hipError_t scratch_address(void** out);
 
 }  // namespace fa

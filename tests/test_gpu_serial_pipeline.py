@@ -1,0 +1,97 @@
+"""The pipelined bf16 forward against its serial debug build, bit for bit.
+
+libfa_serial.so is libfa.so with the bf16 forward's loop in its serial form:
+one key tile at a time through a single LDS slot, a full workgroup barrier on
+each side of every copy, no overlap of copies, score products, softmax and
+output products.  The arithmetic of each row is the same in both (the same
+instructions in the same order), so any difference exposes a hazard in the
+pipelined schedule: a slot overwritten while a wavefront still reads it, a
+missing wait, a prefetch of the wrong tile.  This is the check for races that
+a comparison against the oracle, within a tolerance, could miss.
+"""
+import ctypes
+
+import pytest
+import torch
+
+import synthetic
+from tests import gpu_checks as G
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (B, H, N, d, causal): ragged tails, one tile, several tiles, several query blocks
+    (1, 2, 1, 128, True),
+    (1, 2, 33, 128, False),
+    (1, 3, 300, 128, True),
+    (2, 2, 700, 128, False),
+    (1, 2, 1000, 64, True),
+    (1, 3, 513, 64, False),
+]
+
+
+def _fwd(lib, q, k, v, causal, scale):
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d, int(causal),
+                    scale, 1, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, st
+    return o, lse
+
+
+def _split(lib, q, k, v, causal, scale, n_splits):
+    B, H, N, d = q.shape
+    o = torch.empty((n_splits, B, H, N, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((n_splits, B, H, N), dtype=torch.float32, device=q.device)
+    st = lib.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, N, d, 0,
+                          0, N, n_splits, int(causal), scale, 1,
+                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, st
+    return o, lse
+
+
+@pytest.fixture(scope="module")
+def libs(fa):
+    return fa.load_library(), fa.load_serial_library()
+
+
+def _same(name, a, b):
+    oa, la = a
+    ob, lb = b
+    torch.cuda.synchronize()
+    eq_o = torch.equal(oa, ob)
+    eq_l = torch.equal(la, lb)
+    if not (eq_o and eq_l):
+        G.log(f"  {name}: max|dO| {(oa.float() - ob.float()).abs().max().item():.3e} "
+              f"max|dLSE| {(la - lb).abs().max().item():.3e}")
+    assert eq_o and eq_l, name
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}N{}d{}{}".format(*c[:4], "c" if c[4] else ""))
+def test_pipelined_equals_serial(libs, case):
+    B, H, N, d, causal = case
+    G.log(f"case serial-vs-pipelined B{B} H{H} N{N} d{d} causal={causal}")
+    q, k, v = (x.cuda() for x in synthetic.draw_qkv(B, H, N, d, seed=500 + N, dtype="bf16"))
+    for scale in (d ** -0.5, 0.5, -0.15):
+        _same(f"scale {scale}", _fwd(libs[0], q, k, v, causal, scale), _fwd(libs[1], q, k, v, causal, scale))
+
+
+@pytest.mark.parametrize("name", ["bf16_causal_b4h16n2048d128", "bf16_b16h16n1024d64"])
+def test_pipelined_equals_serial_workload(libs, name):
+    """Whole launches of the bench workloads, every output compared."""
+    w = synthetic.workload(name)
+    G.log(f"case serial-vs-pipelined {w.name}")
+    q, k, v, _ = synthetic.workload_inputs(w)
+    q, k, v = q.cuda(), k.cuda(), v.cuda()
+    _same(w.name, _fwd(libs[0], q, k, v, w.causal, w.scale), _fwd(libs[1], q, k, v, w.causal, w.scale))
+
+
+def test_pipelined_equals_serial_split(libs):
+    """The key-range (split) form of the same kernel: 200 queries, 4 ranges."""
+    B, H, N, d = 1, 2, 600, 128
+    G.log(f"case serial-vs-pipelined split B{B} H{H} N{N} d{d}")
+    q, k, v = (x.cuda() for x in synthetic.draw_qkv(B, H, N, d, seed=611, dtype="bf16"))
+    for causal in (False, True):
+        _same(f"split causal={causal}", _split(libs[0], q, k, v, causal, d ** -0.5, 4),
+              _split(libs[1], q, k, v, causal, d ** -0.5, 4))

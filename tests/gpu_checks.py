@@ -162,3 +162,45 @@ def fp8_errors(o_gpu, lse_gpu, q8, k8, v8t, qs, ks, vs, causal, scale, heads, ro
         worst_abs = max(worst_abs, float(err.max()))
         worst_lse = max(worst_lse, float((np.abs(lg - l_ref[0, 0]) / np.maximum(1.0, np.abs(l_ref[0, 0]))).max()))
     return worst_rel, worst_abs, worst_lse
+
+
+# Backward, element by element: each gradient element is a sum of terms, and rounding
+# P and dS to bf16, the fp32 accumulations and the final bf16 rounding each move it by
+# a fraction of the sum of the magnitudes of its terms:
+#   dV_jc = sum_i P_ij dO_ic                -> sum_i P_ij |dO_ic|
+#   dQ_ic = scale sum_j dS_ij K_jc          -> |scale| sum_j |dS_ij| |K_jc|
+#   dK_jc = scale sum_i dS_ij Q_ic          -> |scale| sum_i |dS_ij| |Q_ic|
+# (the same construction as the FP8 G5b gate).  The floor, 1e-3 of the tensor's largest
+# such sum (at least 1e-3), covers the fp32 cancellation in dP - D, whose rounding does
+# not shrink with |dP - D|.  The bound is the forward's bf16 budget.
+BWD_ELEM_TOL = 2e-2
+
+
+def bwd_term_scales(q, k, v, do, o, causal: bool, scale: float, chunk: int = 2048):
+    """(mQ, mK, mV): the sums of term magnitudes above, float64 [B, H, N, d], with D
+    from the given output o; query rows in chunks of `chunk` (bounded memory)."""
+    q, k, v, do, o = (to_np(x) for x in (q, k, v, do, o))
+    B, H, N, d = q.shape
+    mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, N, chunk):
+                rows = np.arange(r0, min(N, r0 + chunk))
+                p = A.probabilities(q[b, h], k[b, h], causal, scale, rows=rows)
+                dp = do[b, h, rows] @ v[b, h].T
+                dd = (do[b, h, rows] * o[b, h, rows]).sum(axis=1, keepdims=True)
+                ds = np.abs(p * (dp - dd))
+                mv[b, h] += p.T @ np.abs(do[b, h, rows])
+                mq[b, h, rows] = abs(scale) * (ds @ np.abs(k[b, h]))
+                mk[b, h] += abs(scale) * (ds.T @ np.abs(q[b, h, rows]))
+    return mq, mk, mv
+
+
+def bwd_elem_errors(got, ref, scales) -> list:
+    """max over elements of |g - g_ref| / (term scale + floor), per gradient tensor."""
+    out = []
+    for g, r, m in zip(got, ref, scales):
+        g = to_np(g)
+        floor = 1e-3 * max(1.0, float(m.max()))
+        out.append(float((np.abs(g - r) / (m + floor)).max()))
+    return out

@@ -2,12 +2,14 @@
 
 The kernel recomputes P from the forward's fp32 LSE, takes D = rowsum(dO * O)
 from the bf16 O it is given, rounds P and dS to bf16 for the products that use
-them and rounds the gradients to bf16 once.  The bound compares each gradient
-tensor of a head normwise, max |g - g_ref| / max(1, max |g_ref|) <= 2e-2: the
-same budget as the bf16 forward output (whose magnitude is O(1)), here relative
-to the tensor's largest entry where that exceeds 1, because gradient magnitudes
-scale with the scale, N and the inputs (with one key, dQ and dK vanish
-exactly and only rounding remains).
+them and rounds the gradients to bf16 once.  Two bounds, both the bf16 budget
+of the forward output (2e-2):
+  * element by element, |g - g_ref| against the sum of the magnitudes of the
+    terms that make up that element (tests/gpu_checks.py, bwd_term_scales), the
+    analogue of the FP8 forward's G5b gate;
+  * normwise, max |g - g_ref| / max(1, max |g_ref|) per gradient tensor of a head
+    (gradient magnitudes scale with the scale, N and the inputs; with one key,
+    dQ and dK vanish exactly and only rounding remains).
 
 Each case checks against the oracle with D taken from the same bf16 O (the
 kernel's own arithmetic) and, where stated, against the exact oracle (end to
@@ -44,6 +46,13 @@ def _errors(got, ref):
     return out
 
 
+def _elem(got, ref, q, k, v, do, o, causal, scale):
+    """Element-wise errors against the term scales (D from the given O, like ref)."""
+    e = G.bwd_elem_errors(got, ref, G.bwd_term_scales(q, k, v, do, o, causal, scale))
+    G.log(f"  element-wise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
+    return e
+
+
 # B*H a multiple of 8 takes the grouped block order of non-causal launches
 SMALL = [(1, 2, n, d) for n in (1, 7, 64, 100, 129, 300, 513) for d in (64, 128)] + [(2, 4, 300, 128), (2, 8, 129, 64)]
 
@@ -56,10 +65,12 @@ def test_backward_small(fa, shape, causal):
     q, k, v = synthetic.draw_qkv(B, H, N, d, seed=N * 7 + d, dtype="bf16")
     do = synthetic.draw_qkv(B, H, N, d, seed=N * 7 + d + 1, dtype="bf16")[0]
     got, o = _grads(fa, q, k, v, do, causal, d ** -0.5, with_o=True)
-    e = _errors(got, A.backward(q, k, v, do, causal, d ** -0.5, o=o))
+    ref = A.backward(q, k, v, do, causal, d ** -0.5, o=o)
+    e = _errors(got, ref)
     x = _errors(got, A.backward(q, k, v, do, causal, d ** -0.5))
     G.log(f"  normwise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e} (exact O: {max(x):.2e})")
     assert max(e) <= TOL and max(x) <= TOL
+    assert max(_elem(got, ref, q, k, v, do, o, causal, d ** -0.5)) <= G.BWD_ELEM_TOL
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -81,6 +92,7 @@ def test_backward_scales(fa, scale, d, causal):
         e = _errors(got, ref)
     G.log(f"  normwise errors {['%.2e' % x for x in e]}")
     assert max(e) <= TOL
+    assert max(_elem(got, ref, q, k, v, do, o, causal, scale)) <= G.BWD_ELEM_TOL
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -109,10 +121,12 @@ def test_backward_few_keys_large_scale(fa, d):
     q, k, v = synthetic.draw_qkv(1, 1, 2, d, seed=578167, dtype="bf16")
     do = synthetic.draw_qkv(1, 1, 2, d, seed=578169, dtype="bf16")[0]
     got, o = _grads(fa, q, k, v, do, False, 0.3, with_o=True)
-    e = _errors(got, A.backward(q, k, v, do, False, 0.3, o=o))
+    ref = A.backward(q, k, v, do, False, 0.3, o=o)
+    e = _errors(got, ref)
     x = _errors(got, A.backward(q, k, v, do, False, 0.3))
     G.log(f"  normwise errors against D from the given O {max(e):.2e}, against the exact O {max(x):.2e}")
     assert max(e) <= TOL
+    assert max(_elem(got, ref, q, k, v, do, o, False, 0.3)) <= G.BWD_ELEM_TOL
 
 
 def test_backward_full_size_heads(fa):
@@ -128,6 +142,8 @@ def test_backward_full_size_heads(fa):
         e = _errors([x[sl] for x in got], ref)
         G.log(f"  head ({b},{h}) normwise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
         assert max(e) <= TOL
+        assert max(_elem([x[sl] for x in got], ref, q[sl], k[sl], v[sl], do[sl], o[sl], w.causal, w.scale)) <= \
+            G.BWD_ELEM_TOL
     for _ in range(2):  # no atomics: bitwise reproducible
         again = _grads(fa, q, k, v, do, w.causal, w.scale)
         assert all(torch.equal(x, y) for x, y in zip(got, again))
@@ -147,3 +163,5 @@ def test_backward_long_sequence_head(fa):
     e = _errors([x[sl] for x in got], ref)
     G.log(f"  head ({b},{h}) normwise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
     assert max(e) <= TOL
+    assert max(_elem([x[sl] for x in got], ref, q[sl], k[sl], v[sl], do[sl], o[sl], w.causal, w.scale)) <= \
+        G.BWD_ELEM_TOL

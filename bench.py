@@ -221,6 +221,32 @@ def time_loop(fn, iters: int) -> float:
     return e0.elapsed_time(e1) / 1e3 / iters
 
 
+def graph_time(fn, iters: int, reps: int = 20) -> float:
+    """Seconds per call of fn with `iters` calls captured in one HIP graph and the graph
+    replayed `reps` times: the GPU time of back-to-back steps without the host's
+    per-launch cost (which bounds the plain loop for microsecond-scale launches)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(iters):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        g.replay()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / (iters * reps)
+
+
 def warm_up(fn, steps: int, min_s: float) -> tuple[int, float]:
     """Untimed warm-up: at least `steps` calls of fn, continued until min_s seconds of
     back-to-back work have passed.  The chip raises its clock over tens of
@@ -491,6 +517,8 @@ def main():
                     help="time the backward pass (fa_bwd) of a bf16 workload instead of the forward")
     ap.add_argument("--split-kv", action="store_true",
                     help="time a decode-shaped split-KV forward (one fa_fwd_split launch + fa_merge)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the steps replayed from a HIP graph (launch-bound workloads)")
     ap.add_argument("--no-calibration", dest="calibrate", action="store_false",
                     help="skip the MFMA-only and copy calibration kernels")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -531,7 +559,7 @@ def main():
         return bench_backward(fa, w, dev, args)
     with SclkSampler() as sclk:
         main_m = measure_forward(fa, w, dev, args.steps, args.warmup, args.min_warmup_s, args.windows,
-                                 args.cold_cache)
+                                 args.cold_cache, args.graph)
         extra = {}
         if args.extras and w.name == DEFAULT_WORKLOAD:
             for name in EXTRA_WORKLOADS:
@@ -553,7 +581,7 @@ def main():
         "ms_per_step": r["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": r["config"], "frac_of_peak": r["frac_of_peak"], "wall_s_timed": main_m["wall_s"],
-        "windows": r["windows"], "cold_cache": r["cold_cache"],
+        "windows": r["windows"], "cold_cache": r["cold_cache"], "graph": r.get("graph"),
         "roofline": r["roofline"], "cpu_baseline": cpu,
         "sclk": sclk.summary(),
         "calibration": calib,
@@ -562,7 +590,8 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def measure_forward(fa, w, dev, steps: int, warmup: int, min_warmup_s: float, windows: int, cold: bool) -> dict:
+def measure_forward(fa, w, dev, steps: int, warmup: int, min_warmup_s: float, windows: int, cold: bool,
+                    graph: bool = False) -> dict:
     """Times `steps` back-to-back steps of a forward workload after the warm-up,
     then the attention kernel alone (and, for fp8, the pre-pass alone)."""
     step, parts = make_step(fa, w, dev)
@@ -573,6 +602,7 @@ def measure_forward(fa, w, dev, steps: int, warmup: int, min_warmup_s: float, wi
     wall = time.perf_counter() - t0
     wins = sorted(extra_windows(step, steps, windows)) if windows > 0 else []
     cold_s = cold_cache_time(step, min(steps, 50), dev) if cold else None
+    graph_s = graph_time(step, min(steps, 100)) if graph else None
     pre_sec = None
     if parts is None:
         k_sec = sec
@@ -580,7 +610,8 @@ def measure_forward(fa, w, dev, steps: int, warmup: int, min_warmup_s: float, wi
         prepass, attn = parts
         pre_sec = time_loop(prepass, steps)
         k_sec = time_loop(attn, steps)
-    return {"sec": sec, "k_sec": k_sec, "pre_sec": pre_sec, "wins": wins, "cold": cold_s, "warmup": wn,
+    return {"sec": sec, "k_sec": k_sec, "pre_sec": pre_sec, "wins": wins, "cold": cold_s, "graph": graph_s,
+            "warmup": wn,
             "warmup_s": round(ws, 3), "wall_s": round(wall, 4), "steps": steps}
 
 
@@ -611,6 +642,11 @@ def forward_record(w, m: dict) -> dict:
             "ms_per_step_median": round(statistics.median(wins) * 1e3, 5), "ms_per_step_best": round(wins[0] * 1e3, 5),
             "value_median": round(w.flops() / statistics.median(wins) / 1e12, 2),
             "value_best": round(w.flops() / wins[0] / 1e12, 2)}
+    if m.get("graph") is not None:
+        gs = m["graph"]
+        eprint(f"{w.name}: graph replay {gs * 1e6:.2f} us per step ({w.flops() / gs / 1e12:.2f} TFLOP/s)")
+        rec["graph"] = {"ms_per_step": round(gs * 1e3, 6), "value": round(w.flops() / gs / 1e12, 3),
+                        "note": "min(steps, 100) steps captured in one HIP graph, replayed 20 times"}
     if m["cold"] is not None:
         rec["cold_cache"] = {"ms_per_step_median": round(m["cold"] * 1e3, 5),
                              "value": round(w.flops() / m["cold"] / 1e12, 2),

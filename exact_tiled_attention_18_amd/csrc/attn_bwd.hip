@@ -74,32 +74,71 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // holds row (r & 7) + 8 g + 2 (r & 8) of the unpermuted operand
 __device__ __forceinline__ int row_of_reg(int r, int g) { return (r & 7) + 8 * g + 2 * (r & 8); }
 
+// LDS operand tiles: kT rows of S bytes.  A tile is read both ways: as rows
+// (16-byte reads, 16 lanes on 16 different rows) and transposed (ds_read_b64_tr_b16,
+// 8 lanes on each of 4 consecutive rows, 64 bytes of each).  The stride S = 2 D + 64
+// puts 4 consecutive rows in 4 different 16-bank windows, which the transposed reads
+// need; rows 4 apart then share a window, so the 16-byte piece p of row R is stored
+// at piece p ^ swz(R), swz(R) = (R >> 2) & 3: the 4 rows that share a window use 4
+// different 4-bank slots of it, and both kinds of read are free of bank conflicts.
+// (The plain layout had 4-way conflicts on every row read: 2.8e7 conflict cycles per
+// launch in each of the d = 128 gradient kernels at B4 H16 N2048.)
 template <int D>
 struct Tile {
-  static constexpr int S = D * 2 + 64;         // row stride (bytes): conflict-free transposing reads
+  static constexpr int S = D * 2 + 64;         // row stride (bytes)
   static constexpr int BYTES = kT * S;
   static constexpr int PIECES = kT * D * 2 / 16;  // 16-byte pieces per tile
 };
 
-// 8 bf16 of row `row` of a tile, columns 16 ks + 8 g .. +7 (an A operand with
-// permuted rows, or a row-major B operand)
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+// byte offset of 16-byte piece `piece` of row `row`
 template <int D>
-__device__ __forceinline__ bf16x8 read_row(const char* tile, int row, int ks, int g) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * Tile<D>::S + ks * 32 + g * 16);
+__device__ __forceinline__ int piece_off(int row, int piece) {
+  return row * Tile<D>::S + ((piece ^ swz(row)) << 4);
+}
+
+// A lane's row reads: pieces 2 ks + g of one row.  With c = swz(row), piece
+// (2 ks + g) ^ c lies at byte 32 ks + 32 c1 + 16 (g ^ c0) for even ks and at
+// 32 ks - 32 c1 + 16 (g ^ c0) for odd ks (c = 2 c1 + c0), so each parity has a
+// per-lane base and ks stays a constant offset.
+struct RowRd {
+  int even, odd;
+};
+template <int D>
+__device__ __forceinline__ RowRd row_reader(int row, int g) {
+  const int c = swz(row), b = row * Tile<D>::S + 16 * (g ^ (c & 1));
+  return RowRd{b + 32 * (c >> 1), b - 32 * (c >> 1)};
+}
+
+// 8 bf16 of the lane's row, columns 16 ks + 8 g .. +7 (an A operand with permuted
+// rows, or a row-major B operand)
+template <int D>
+__device__ __forceinline__ bf16x8 read_row(const char* tile, const RowRd& rr, int ks) {
+  return *reinterpret_cast<const bf16x8*>(tile + ((ks & 1) ? rr.odd : rr.even) + ks * 32);
+}
+
+// A lane's transposed reads: lane k of each 16-lane group points at row
+// 8 (group / 2) + k / 4 (and 4 rows further for the second half), 8 bytes at column
+// byte 32 (group % 2) + 8 (k % 4) of a 64-byte window; the swizzle moves pieces
+// within the window only, so the window (db) and the 16-row step (mm) stay
+// constant offsets.
+struct TrRd {
+  int lo, hi;
+};
+template <int D>
+__device__ __forceinline__ TrRd tr_reader(int lane) {
+  const int grp16 = lane >> 4, l16 = lane & 15;
+  const int r = 8 * (grp16 >> 1) + (l16 >> 2), q = 2 * (grp16 & 1) + ((l16 & 3) >> 1), h = 8 * (l16 & 1);
+  return TrRd{r * Tile<D>::S + 16 * (q ^ swz(r)) + h, (r + 4) * Tile<D>::S + 16 * (q ^ swz(r + 4)) + h};
 }
 
 // the transposed A operand: rows d of block db, k = tile rows 16 mm + 8 g' .. +7
 template <int D>
-__device__ __forceinline__ bf16x8 read_tr(const char* tile, int tr_off, int db, int mm) {
-  const char* pa = tile + tr_off + (mm * 16) * Tile<D>::S + db * 64;
-  const v4i16 lo = tr_read(pa), hi = tr_read(pa + 4 * Tile<D>::S);
+__device__ __forceinline__ bf16x8 read_tr(const char* tile, const TrRd& tr, int db, int mm) {
+  const char* pa = tile + (mm * 16) * Tile<D>::S + db * 64;
+  const v4i16 lo = tr_read(pa + tr.lo), hi = tr_read(pa + tr.hi);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-template <int D>
-__device__ __forceinline__ int tr_offset(int lane) {
-  const int grp16 = lane >> 4, l16 = lane & 15;
-  return (8 * (grp16 >> 1) + (l16 >> 2)) * Tile<D>::S + (16 * (grp16 & 1) + 4 * (l16 & 3)) * 2;
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
@@ -176,9 +215,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const uint16_t* __restrict_
   const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, N * D * 2, kRsrcWord3);
   const bool copier = tid < T::PIECES;
   const int prow = (tid % T::PIECES) / (D / 8), pcol = (tid % (D / 8)) * 16;
-  const int ld_off = prow * D * 2 + pcol, st_off = prow * T::S + pcol;
-  const int krow = permuted_row(li);
-  const int tr_off = tr_offset<D>(lane);
+  const int ld_off = prow * D * 2 + pcol, st_off = piece_off<D>(prow, pcol / 16);
+  const RowRd krow = row_reader<D>(permuted_row(li), g);
+  const TrRd tr_off = tr_reader<D>(lane);
 
   bf16x8 qf[DK], df[DK];
 #pragma unroll
@@ -220,8 +259,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(const uint16_t* __restrict_
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
-      st = mfma(read_row<D>(kbuf(cur), krow, ks, g), qf[ks], st);
-      dpt = mfma(read_row<D>(vbuf(cur), krow, ks, g), df[ks], dpt);
+      st = mfma(read_row<D>(kbuf(cur), krow, ks), qf[ks], st);
+      dpt = mfma(read_row<D>(vbuf(cur), krow, ks), df[ks], dpt);
     }
     // dS^T = P^T * (dP^T - D), keys masked where not visible
     float ds[16];
@@ -271,7 +310,9 @@ struct DqPipe {
   char* kv;     // K buffers at 0 .. NB-1, V buffers at NB .. 2 NB - 1 (BYTES each)
   char* dos;    // dO rows of the workgroup's queries, stride DS
   __amdgpu_buffer_rsrc_t krs, vrs;
-  int N, g, li, qi, qloc, krow, tr_off, ld_off, st_off;
+  int N, g, li, qi, qloc, ld_off, st_off;
+  RowRd krow;
+  TrRd tr_off;
   bool copier;
   float c, lse2, dd;
 
@@ -288,8 +329,8 @@ struct DqPipe {
     *reinterpret_cast<uint4*>(vbuf(b) + st_off) = sv;
   }
   __device__ __forceinline__ void read_sdp(int slot, int ch, int bn) {
-    opk[slot] = read_row<D>(kbuf(bn), krow, ch, g);
-    opv[slot] = read_row<D>(vbuf(bn), krow, ch, g);
+    opk[slot] = read_row<D>(kbuf(bn), krow, ch);
+    opv[slot] = read_row<D>(vbuf(bn), krow, ch);
     opd[slot] = *reinterpret_cast<const bf16x8*>(dos + qloc * DS + ch * 32 + g * 16);
   }
   __device__ __forceinline__ void read_kt(int slot, int ch, int bo) {
@@ -397,9 +438,9 @@ __global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __rest
   w.copier = tid < T::PIECES;
   const int prow = (tid % T::PIECES) / (D / 8), pcol = (tid % (D / 8)) * 16;
   w.ld_off = prow * D * 2 + pcol;
-  w.st_off = prow * T::S + pcol;
-  w.krow = permuted_row(w.li);
-  w.tr_off = tr_offset<D>(lane);
+  w.st_off = piece_off<D>(prow, pcol / 16);
+  w.krow = row_reader<D>(permuted_row(w.li), w.g);
+  w.tr_off = tr_reader<D>(lane);
 
   // this lane's query: Q' fragments in registers, its dO row halves into LDS
 #pragma unroll
@@ -438,8 +479,8 @@ __global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __rest
     for (int r = 0; r < 16; ++r) w.st[0][r] = w.dpt[0][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
-      w.st[0] = mfma(read_row<D>(w.kbuf(0), w.krow, ks, w.g), w.qf[ks], w.st[0]);
-      w.dpt[0] = mfma(read_row<D>(w.vbuf(0), w.krow, ks, w.g),
+      w.st[0] = mfma(read_row<D>(w.kbuf(0), w.krow, ks), w.qf[ks], w.st[0]);
+      w.dpt[0] = mfma(read_row<D>(w.vbuf(0), w.krow, ks),
                       *reinterpret_cast<const bf16x8*>(dos + w.qloc * W::DS + ks * 32 + w.g * 16), w.dpt[0]);
     }
     w.load(2);
@@ -501,10 +542,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     const int piece = tid + 256 * i;
     const int prow = piece / (D / 8), pcol = (piece % (D / 8)) * 16;
     ld_off[i] = prow * D * 2 + pcol;
-    st_off[i] = prow * T::S + pcol;
+    st_off[i] = piece_off<D>(prow, pcol / 16);
   }
-  const int qrow = permuted_row(li);
-  const int tr_off = tr_offset<D>(lane);
+  const RowRd qrow = row_reader<D>(permuted_row(li), g);
+  const TrRd tr_off = tr_reader<D>(lane);
 
   bf16x8 kf[DK], vf[DK];
 #pragma unroll
@@ -560,8 +601,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
     f32x16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
-      s = mfma(read_row<D>(qbuf(cur), qrow, ks, g), kf[ks], s);
-      dp = mfma(read_row<D>(dbuf(cur), qrow, ks, g), vf[ks], dp);
+      s = mfma(read_row<D>(qbuf(cur), qrow, ks), kf[ks], s);
+      dp = mfma(read_row<D>(dbuf(cur), qrow, ks), vf[ks], dp);
     }
     // LSE and D of this lane's 16 queries (two runs of 8)
     float ls[16], dl[16];
@@ -635,7 +676,9 @@ struct DkDv {
   __amdgpu_buffer_rsrc_t qrs, drs;
   const float* lse_h;
   const float* delta_h;
-  int N, tid, g, li, kj, qrow, tr_off;
+  int N, tid, g, li, kj;
+  RowRd qrow;
+  TrRd tr_off;
   int ld_off[kPer], st_off[kPer];
   float c;  // scale * log2(e), signed: Q enters unchanged
 
@@ -699,8 +742,8 @@ struct DkDv {
   }
   // operands of chunk ch: S/dP operands of the tile in buffer bn, dV/dK operands of buffer bo
   __device__ __forceinline__ void read_sdp(int slot, int ch, int bn) {
-    opq[slot] = read_row<D>(qbuf(bn), qrow, ch, g);
-    opd[slot] = read_row<D>(dbuf(bn), qrow, ch, g);
+    opq[slot] = read_row<D>(qbuf(bn), qrow, ch);
+    opd[slot] = read_row<D>(dbuf(bn), qrow, ch);
   }
   __device__ __forceinline__ void read_grad(int slot, int ch, int bo) {
     opv[slot] = read_tr<D>(dbuf(bo), tr_off, ch % DB, ch / DB);
@@ -800,10 +843,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
     const int piece = w.tid + 256 * i;
     const int prow = piece / (D / 8), pcol = (piece % (D / 8)) * 16;
     w.ld_off[i] = prow * D * 2 + pcol;
-    w.st_off[i] = prow * T::S + pcol;
+    w.st_off[i] = piece_off<D>(prow, pcol / 16);
   }
-  w.qrow = permuted_row(w.li);
-  w.tr_off = tr_offset<D>(lane);
+  w.qrow = row_reader<D>(permuted_row(w.li), w.g);
+  w.tr_off = tr_reader<D>(lane);
 
 #pragma unroll
   for (int ks = 0; ks < DK; ++ks) {
@@ -841,8 +884,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
     for (int r = 0; r < 16; ++r) w.s[0][r] = w.dp[0][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
-      w.s[0] = mfma(read_row<D>(w.qbuf(0), w.qrow, ks, w.g), w.kf[ks], w.s[0]);
-      w.dp[0] = mfma(read_row<D>(w.dbuf(0), w.qrow, ks, w.g), w.vf[ks], w.dp[0]);
+      w.s[0] = mfma(read_row<D>(w.qbuf(0), w.qrow, ks), w.kf[ks], w.s[0]);
+      w.dp[0] = mfma(read_row<D>(w.dbuf(0), w.qrow, ks), w.vf[ks], w.dp[0]);
     }
     w.load(t0 + 2);
     w.read_grad(0, 0, 3);

@@ -80,6 +80,7 @@ namespace {
 constexpr int kBc = 32;           // keys per tile
 constexpr int kSlots = 3;         // LDS slots per operand
 constexpr float kRescaleSlack = 8.f;
+constexpr float kSumBound = 256.f;  // 2^kRescaleSlack
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -137,6 +138,7 @@ struct Attn {
   bf16x8 kop[2], vop[2];   // operand prefetch, by chunk parity
   uint4 stg_k[Ly::CHUNKS], stg_v[Ly::CHUNKS];
   float m[kQB], l[kQB], lh[kQB], alpha[kQB], msub[kQB], mx[kQB], rs[kQB];
+  float ex[kQB][16];       // probabilities of the tile being softmaxed (its scores stay in sbuf)
 
   // ---- per-workgroup constants
   __amdgpu_buffer_rsrc_t krs, vrs;  // this head's K and V; reads past N return zeros
@@ -222,8 +224,7 @@ struct Attn {
     // 0 when m was -inf, exactly 1 when unchanged (also for rows with no visible key yet)
     alpha[qb] = GUARD && m_new == -kInf ? 1.f : exp2_fast(m[qb] - m_new);
     m[qb] = m_new;
-    l[qb] *= alpha[qb];
-    lh[qb] *= alpha[qb];
+    lh[qb] *= alpha[qb];  // (l takes its factor with the tile's sum, in pack)
     msub[qb] = GUARD && m_new == -kInf ? 0.f : m_new;
   }
   // exponentials of scores e0 .. e0 + n - 1 (n a power of two dividing 16, so one
@@ -235,7 +236,7 @@ struct Attn {
 #pragma unroll
     for (int i = 0; i < n; ++i) {
       t[i] = exp2_fast(fmaf(sbuf[B][qb][r0 + i], c, -msub[qb]));  // masked: exp2(-inf) = 0
-      sbuf[B][qb][r0 + i] = t[i];
+      ex[qb][r0 + i] = t[i];
     }
 #pragma unroll
     for (int w = n / 2; w >= 1; w /= 2)
@@ -249,10 +250,10 @@ struct Attn {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint4 wv;
-      wv.x = pack_bf16x2(sbuf[B][qb][8 * h + 0], sbuf[B][qb][8 * h + 1]);
-      wv.y = pack_bf16x2(sbuf[B][qb][8 * h + 2], sbuf[B][qb][8 * h + 3]);
-      wv.z = pack_bf16x2(sbuf[B][qb][8 * h + 4], sbuf[B][qb][8 * h + 5]);
-      wv.w = pack_bf16x2(sbuf[B][qb][8 * h + 6], sbuf[B][qb][8 * h + 7]);
+      wv.x = pack_bf16x2(ex[qb][8 * h + 0], ex[qb][8 * h + 1]);
+      wv.y = pack_bf16x2(ex[qb][8 * h + 2], ex[qb][8 * h + 3]);
+      wv.z = pack_bf16x2(ex[qb][8 * h + 4], ex[qb][8 * h + 5]);
+      wv.w = pack_bf16x2(ex[qb][8 * h + 6], ex[qb][8 * h + 7]);
       pbuf[B][qb][h] = __builtin_bit_cast(bf16x8, wv);
       h_acc[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.x), ones, h_acc[h], false);
       h_acc[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.y), ones, h_acc[h], false);
@@ -260,7 +261,9 @@ struct Attn {
       h_acc[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wv.w), ones, h_acc[h], false);
     }
     lh[qb] = h_acc[0] + h_acc[1];
-    l[qb] += rs[qb];
+    // one explicit fused step, so that every path (pipelined, serial, and the
+    // steady steps that skip the maximum) rounds the fp32 sum the same way
+    l[qb] = fmaf(l[qb], alpha[qb], rs[qb]);
     // The probabilities and sums are next read after the step's conditional rescale
     // of O; without a use here the compiler's IR sinking moves the whole softmax
     // (exponentials included) past that branch, out of reach of the step's MFMAs.
@@ -269,14 +272,24 @@ struct Attn {
     asm volatile("" ::"v"(p0), "v"(p1), "v"(lh[qb]), "v"(l[qb]));
   }
   // slice ch of the softmax work: mask and row max, shift, the 16*kQB exponentials
-  // spread over the middle chunks, packing at the end
+  // spread over the middle chunks, packing at the end.
+  // Unmasked steady steps (GUARD false) first take the exponentials under the
+  // current shift, without the row maximum: the shift would move only if a score
+  // exceeded it by more than kRescaleSlack, i.e. only if a probability exceeded
+  // 2^kRescaleSlack, and a lane's probabilities are bounded by their sum.  So when
+  // every lane's sum stays within 2^kRescaleSlack the shift stays, the correction
+  // factor is 1 and the step is exactly the one the maximum would have given; when
+  // some sum exceeds it (rare once the shift has settled; also +inf and NaN sums),
+  // the wavefront takes the full path: the row maximum of the scores (still in
+  // sbuf), the shift rule, and the exponentials again.
   template <bool GUARD>
   __device__ __forceinline__ void softmax_slice(int ch, int B, int t) {
+    constexpr bool FAST = !GUARD;
     constexpr int E = 16 * kQB;
     constexpr int first_exp = NCH == 8 ? 2 : 1;       // chunks [first_exp, last_exp) hold exponentials
     constexpr int last_exp = NCH == 8 ? 6 : 3;
     constexpr int per = (E + (last_exp - first_exp) - 1) / (last_exp - first_exp);
-    if (ch == 0) {
+    if (ch == 0 && !FAST) {
       if (GUARD) mask_scores(B, t);
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) row_max(B, qb);
@@ -285,12 +298,36 @@ struct Attn {
         for (int qb = 0; qb < kQB; ++qb) new_shift<GUARD>(qb);
       }
     }
-    if (NCH == 8 && ch == 1) {
+    if (NCH == 8 && ch == 1 && !FAST) {
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) new_shift<GUARD>(qb);
     }
+    if (FAST && ch == (NCH == 8 ? 1 : 0)) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) alpha[qb] = 1.f;
+    }
     static_assert(per * (last_exp - first_exp) == E && 16 % per == 0, "whole power-of-two runs of one query block");
     if (ch >= first_exp && ch < last_exp) exps<per>(B, (ch - first_exp) * per);
+    if (FAST && ch == NCH - 2) {
+      bool big = false;
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) big |= !(rs[qb] <= kSumBound);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(big) != 0, 0)) {
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) {
+          row_max(B, qb);
+          new_shift<false>(qb);
+        }
+        // the exponentials again, in the same runs (the same order of the row sum)
+#pragma unroll
+        for (int e0 = 0; e0 < E; e0 += per) exps<per>(B, e0);
+      }
+      // keep the probabilities where the fast path left them (no copies on that path)
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) asm volatile("" : "+v"(ex[qb][r]), "+v"(ex[qb][r + 1]), "+v"(ex[qb][r + 2]), "+v"(ex[qb][r + 3]));
+    }
     if (ch == NCH - 2) pack(B, 0);
     if (ch == NCH - 1 && kQB == 2) pack(B, 1);
   }

@@ -286,8 +286,12 @@ struct Attn {
   __device__ __forceinline__ void softmax_slice(int ch, int B, int t) {
     constexpr bool FAST = !GUARD;
     constexpr int E = 16 * kQB;
-    constexpr int first_exp = NCH == 8 ? 2 : 1;       // chunks [first_exp, last_exp) hold exponentials
-    constexpr int last_exp = NCH == 8 ? 6 : 3;
+    // chunks [first_exp, last_exp) hold the exponentials, chunk pack_ch the packing; the
+    // steps that skip the maximum start one chunk earlier (chunk 0 still waits for the
+    // last score product of the previous step): 1.2-1.5 % faster than chunks 2-5 and 6
+    constexpr int first_exp = NCH == 8 ? (FAST ? 1 : 2) : 1;
+    constexpr int last_exp = NCH == 8 ? (FAST ? 5 : 6) : 3;
+    constexpr int pack_ch = NCH == 8 && FAST ? 5 : NCH - 2;
     constexpr int per = (E + (last_exp - first_exp) - 1) / (last_exp - first_exp);
     if (ch == 0 && !FAST) {
       if (GUARD) mask_scores(B, t);
@@ -308,7 +312,7 @@ struct Attn {
     }
     static_assert(per * (last_exp - first_exp) == E && 16 % per == 0, "whole power-of-two runs of one query block");
     if (ch >= first_exp && ch < last_exp) exps<per>(B, (ch - first_exp) * per);
-    if (FAST && ch == NCH - 2) {
+    if (FAST && ch == pack_ch) {
       bool big = false;
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) big |= !(rs[qb] <= kSumBound);
@@ -328,7 +332,7 @@ struct Attn {
 #pragma unroll
         for (int r = 0; r < 16; r += 4) asm volatile("" : "+v"(ex[qb][r]), "+v"(ex[qb][r + 1]), "+v"(ex[qb][r + 2]), "+v"(ex[qb][r + 3]));
     }
-    if (ch == NCH - 2) pack(B, 0);
+    if (ch == pack_ch) pack(B, 0);
     if (ch == NCH - 1 && kQB == 2) pack(B, 1);
   }
 

@@ -95,3 +95,48 @@ def test_pipelined_equals_serial_split(libs):
     for causal in (False, True):
         _same(f"split causal={causal}", _split(libs[0], q, k, v, causal, d ** -0.5, 4),
               _split(libs[1], q, k, v, causal, d ** -0.5, 4))
+
+
+def _growing_keys(B, H, N, d, seed, growth):
+    """K rows scaled by 1 + growth * j / N: the row maxima keep rising along the keys, so the
+    steady steps keep finding scores above their shift (the path that recomputes the step)."""
+    q, k, v = synthetic.draw_qkv(B, H, N, d, seed=seed, dtype="bf16")
+    ramp = 1.0 + growth * torch.arange(N, dtype=torch.float32) / N
+    k = (k.float() * ramp[None, None, :, None]).to(torch.bfloat16)
+    return q, k, v
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rising_maxima_take_the_full_step(libs, d):
+    """Scores that keep exceeding the running shift in unmasked steps: the steps that skip
+    the maximum must detect it and redo the step, bit-identical to the serial build and
+    within the bf16 bounds of the oracle."""
+    B, H, N = 1, 2, 1024
+    G.log(f"case rising maxima d={d}")
+    q, k, v = _growing_keys(B, H, N, d, seed=620 + d, growth=6.0)
+    for causal in (False, True):
+        for scale in (d ** -0.5, 0.5):
+            got = _fwd(libs[0], q.cuda(), k.cuda(), v.cuda(), causal, scale)
+            _same(f"rising causal={causal} scale={scale}", got, _fwd(libs[1], q.cuda(), k.cuda(), v.cuda(), causal, scale))
+            eo, el = G.compare_attention(got[0], got[1], q, k, v, causal, scale, "bf16")
+            G.log(f"  causal={causal} scale={scale}: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+            assert eo <= G.TOL["bf16"][0] and el <= G.TOL["bf16"][1]
+
+
+def test_overflowing_jump_takes_the_full_step(libs):
+    """One late key whose score exceeds every earlier one by far more than 128 (log2 units):
+    under the old shift its probability overflows to +inf, which must send the step down the
+    full path; rows that see the key then weight it alone."""
+    B, H, N, d = 1, 1, 700, 128
+    G.log("case overflowing jump")
+    q, k, v = synthetic.draw_qkv(B, H, N, d, seed=640, dtype="bf16")
+    j, i0 = 600, 650
+    k = k.clone()
+    k[0, 0, j] = (q[0, 0, i0].float() * 1.5).to(torch.bfloat16)  # row i0 scores about 1.5 * |q|^2 = 190 on key j
+    for causal in (False, True):
+        got = _fwd(libs[0], q.cuda(), k.cuda(), v.cuda(), causal, 1.0)
+        _same(f"jump causal={causal}", got, _fwd(libs[1], q.cuda(), k.cuda(), v.cuda(), causal, 1.0))
+        assert torch.isfinite(got[0].float()).all() and torch.isfinite(got[1]).all()
+        eo, el = G.compare_attention(got[0], got[1], q, k, v, causal, 1.0, "bf16")
+        G.log(f"  causal={causal}: max|dO| {eo:.3e}  max|dLSE| {el:.3e}")
+        assert eo <= G.TOL["bf16"][0] and el <= G.TOL["bf16"][1]

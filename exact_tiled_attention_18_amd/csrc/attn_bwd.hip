@@ -704,6 +704,21 @@ struct DkDv {
     }
     if (tid < 2 * kT) stat[(b * 2 + tid / kT) * kT + (tid & (kT - 1))] = sstat;
   }
+  // LSE and D of half h of this lane's 16 queries (the queries 8 h .. 8 h + 7 of each
+  // of its two runs of 8) of the tile in buffer b
+  __device__ __forceinline__ void read_stats_half(int b, int h) {
+    const float4* sl = reinterpret_cast<const float4*>(stat + (b * 2) * kT);
+    const float4* sdl = reinterpret_cast<const float4*>(stat + (b * 2 + 1) * kT);
+    const float4 a0 = sl[4 * h + 2 * g], a1 = sl[4 * h + 2 * g + 1];
+    const float4 b0 = sdl[4 * h + 2 * g], b1 = sdl[4 * h + 2 * g + 1];
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      ls[8 * h + r] = av[r];
+      dl[8 * h + r] = bv[r];
+    }
+  }
   // LSE and D of this lane's 16 queries (two runs of 8) of the tile in buffer b
   __device__ __forceinline__ void read_stats(int b) {
     const float4* sl = reinterpret_cast<const float4*>(stat + (b * 2) * kT);
@@ -730,11 +745,20 @@ struct DkDv {
         const int r = e + h;
         const int qr = t * kT + row_of_reg(r, g);
         const bool vis = !G || (qr < N && kj < N && (!CAUSAL || kj <= qr));
-        p2[h] = vis ? exp2_fast(fmaf(s[B][r], c, -ls[r])) : 0.f;
-        d2[h] = p2[h] * (dp[B][r] - dl[r]);
+        // An empty volatile asm on the scores, still in the accumulation registers:
+        // the copies out of them and the vector work after it stay in this chunk
+        // (the scheduler otherwise gathers all 32 copies, or all 16 exponentials, into
+        // one chunk, where they hold up that chunk's MFMAs).
+        float sv = s[B][r], dv = dp[B][r];
+        asm volatile("" : "+a"(sv), "+a"(dv));
+        p2[h] = vis ? exp2_fast(fmaf(sv, c, -ls[r])) : 0.f;
+        d2[h] = p2[h] * (dv - dl[r]);
       }
       pw[B][e >> 1] = pack_bf16x2(p2[0], p2[1]);
       sw[B][e >> 1] = pack_bf16x2(d2[0], d2[1]);
+      // and a use of the packed results here, so that the compiler does not sink the
+      // work towards its uses in the next step
+      asm volatile("" ::"v"(pw[B][e >> 1]), "v"(sw[B][e >> 1]));
     }
   }
   __device__ __forceinline__ bf16x8 word8(const uint32_t (&w)[8], int mm) const {
@@ -751,13 +775,15 @@ struct DkDv {
   }
 
   // one step for tile t in buffer cur (parity B = (t - t0) & 1); the dV/dK operands
-  // of its chunk 0 were read by the previous step (tile t+1's were written before
-  // the last barrier only, so its S/dP operands are read here)
+  // of its chunk 0 and the statistics of tile t were read by the previous step (tile
+  // t+1's were written before the last barrier only, so its S/dP operands are read
+  // here, and its statistics from the middle of the step on, into the registers of
+  // the elements already done).  Tile t+3 is loaded whether or not it exists: past
+  // the last tile the buffer range check returns zeros, which no step uses.
   template <int B, bool G = true>
-  __device__ __forceinline__ void step(int t, int cur, bool more) {
+  __device__ __forceinline__ void step(int t, int cur) {
     const int bn = (cur + 1) % NB, bo = (cur + NB - 1) % NB, bw = (cur + 2) % NB;
     read_sdp(0, 0, bn);
-    read_stats(cur);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[B ^ 1][r] = dp[B ^ 1][r] = 0.f;
 #pragma unroll
@@ -774,8 +800,11 @@ struct DkDv {
       dka[db] = mfma(opk[sl], word8(sw[B ^ 1], mm), dka[db]);
       dp[B ^ 1] = mfma(opd[sl], vf[ch], dp[B ^ 1]);
       grad_slice<B, G>(t, ch * EPC);
+      // the next tile's statistics, into the halves this step has finished with
+      if (ch == DK / 2) read_stats_half(bn, 0);
+      if (ch == DK - 1) read_stats_half(bn, 1);
       if (ch == 1) store(bw);
-      if (ch == 2 && more) load(t + 3);
+      if (ch == 2) load(t + 3);
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
@@ -889,6 +918,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
     }
     w.load(t0 + 2);
     w.read_grad(0, 0, 3);
+    w.read_stats(0);
     int t = t0;
     // four steps per iteration (two parities times the four buffers): buffer indices
     // are constants, so LDS addresses fold into instruction offsets.  Query tiles
@@ -897,10 +927,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
     const int tf = k0 + kBk <= N ? N / kT : 0;
     auto quad = [&](auto guard) {
       constexpr bool G = decltype(guard)::value;
-      w.template step<0, G>(t, 0, t + 3 < nQT);
-      w.template step<1, G>(t + 1, 1, t + 4 < nQT);
-      w.template step<0, G>(t + 2, 2, t + 5 < nQT);
-      w.template step<1, G>(t + 3, 3, t + 6 < nQT);
+      w.template step<0, G>(t, 0);
+      w.template step<1, G>(t + 1, 1);
+      w.template step<0, G>(t + 2, 2);
+      w.template step<1, G>(t + 3, 3);
     };
     if (CAUSAL && t + 3 < nQT) {
       quad(std::true_type{});
@@ -909,11 +939,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
     for (; t + 3 < tf; t += 4) quad(std::false_type{});
     for (; t + 3 < nQT; t += 4) quad(std::true_type{});
     for (; t + 1 < nQT; t += 2) {
-      w.template step<0>(t, (t - t0) % NB, t + 3 < nQT);
-      w.template step<1>(t + 1, (t + 1 - t0) % NB, t + 4 < nQT);
+      w.template step<0>(t, (t - t0) % NB);
+      w.template step<1>(t + 1, (t + 1 - t0) % NB);
     }
     if (t < nQT) {
-      w.template step<0>(t, (t - t0) % NB, t + 3 < nQT);
+      w.template step<0>(t, (t - t0) % NB);
       w.template last<0>((t - t0) % NB);
     } else {
       w.template last<1>((t - 1 - t0) % NB);

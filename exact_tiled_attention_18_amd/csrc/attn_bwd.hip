@@ -339,8 +339,9 @@ struct DqPipe {
   __device__ __forceinline__ bf16x8 word8(const uint32_t (&w)[8], int mm) const {
     return __builtin_bit_cast(bf16x8, make_uint4(w[4 * mm], w[4 * mm + 1], w[4 * mm + 2], w[4 * mm + 3]));
   }
-  // dS^T of score elements [e0, e0 + EPC) of tile t (parity B)
-  template <int B>
+  // dS^T of score elements [e0, e0 + EPC) of tile t (parity B); without G every key
+  // of the tile is visible to every query of the workgroup
+  template <int B, bool G>
   __device__ __forceinline__ void grad_slice(int lim, int e0) {
 #pragma unroll
     for (int e = e0; e < e0 + EPC; e += 2) {
@@ -348,14 +349,17 @@ struct DqPipe {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = e + h;
-        const float pr = row_of_reg(r, g) <= lim ? exp2_fast(fmaf(st[B][r], c, -lse2)) : 0.f;
+        const float pr = !G || row_of_reg(r, g) <= lim ? exp2_fast(fmaf(st[B][r], c, -lse2)) : 0.f;
         d2[h] = pr * (dpt[B][r] - dd);
       }
       dsw[B][e >> 1] = pack_bf16x2(d2[0], d2[1]);
+      // a use of the packed result in this chunk, so that the compiler does not sink the
+      // work towards its use in the next step (and spill on the way)
+      asm volatile("" ::"v"(dsw[B][e >> 1]));
     }
   }
-  template <int B>
-  __device__ __forceinline__ void step(int t, int cur, bool more, int qlim) {
+  template <int B, bool G = true>
+  __device__ __forceinline__ void step(int t, int cur, int qlim) {
     const int bn = (cur + 1) % NB, bo = (cur + NB - 1) % NB, bw = (cur + 2) % NB;
     const int lim = qlim - t * kT;  // last visible key of this lane's query, relative to tile t
     read_sdp(0, 0, bn);
@@ -373,9 +377,9 @@ struct DqPipe {
       acc[db] = mfma(opt[sl], word8(dsw[B ^ 1], mm), acc[db]);
       st[B ^ 1] = mfma(opk[sl], qf[ch], st[B ^ 1]);
       dpt[B ^ 1] = mfma(opv[sl], opd[sl], dpt[B ^ 1]);
-      grad_slice<B>(lim, ch * EPC);
+      grad_slice<B, G>(lim, ch * EPC);
       if (ch == 1) store(bw);
-      if (ch == 2 && more) load(t + 3);
+      if (ch == 2) load(t + 3);  // past the last tile: zeros or unused keys, never read
       __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);  // DS reads
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -488,18 +492,24 @@ __global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __rest
     int t = 0;
     // four steps per iteration (two parities times the four buffers): buffer indices
     // are constants, so LDS addresses fold into instruction offsets
-    for (; t + 3 < nT; t += 4) {
-      w.template step<0>(t, 0, t + 3 < nT, qlim);
-      w.template step<1>(t + 1, 1, t + 4 < nT, qlim);
-      w.template step<0>(t + 2, 2, t + 5 < nT, qlim);
-      w.template step<1>(t + 3, 3, t + 6 < nT, qlim);
-    }
+    // key tiles [0, tf) lie wholly at or before the workgroup's first query (and below
+    // N): they skip the per-element visibility test
+    const int tf = ((CAUSAL ? min(q0, N - 1) : N - 1) + 1) / kT;
+    auto quad = [&](auto guard) {
+      constexpr bool G = decltype(guard)::value;
+      w.template step<0, G>(t, 0, qlim);
+      w.template step<1, G>(t + 1, 1, qlim);
+      w.template step<0, G>(t + 2, 2, qlim);
+      w.template step<1, G>(t + 3, 3, qlim);
+    };
+    for (; t + 3 < tf; t += 4) quad(std::false_type{});
+    for (; t + 3 < nT; t += 4) quad(std::true_type{});
     for (; t + 1 < nT; t += 2) {
-      w.template step<0>(t, t % NB, t + 3 < nT, qlim);
-      w.template step<1>(t + 1, (t + 1) % NB, t + 4 < nT, qlim);
+      w.template step<0>(t, t % NB, qlim);
+      w.template step<1>(t + 1, (t + 1) % NB, qlim);
     }
     if (t < nT) {
-      w.template step<0>(t, t % NB, t + 3 < nT, qlim);
+      w.template step<0>(t, t % NB, qlim);
       w.template last<0>(t % NB);
     } else {
       w.template last<1>((t - 1) % NB);

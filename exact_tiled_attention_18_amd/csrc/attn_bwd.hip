@@ -701,10 +701,12 @@ struct DkDv {
       sq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ld_off[i] + t * kT * D * 2, 0, 0));
       sd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, ld_off[i] + t * kT * D * 2, 0, 0));
     }
-    if (tid < 2 * kT) {
-      const int row = t * kT + (tid & (kT - 1));
-      sstat = row < N ? (tid < kT ? lse_h[row] * kLog2e : delta_h[row]) : 0.f;
-    }
+    // every wavefront loads the tile's 2 kT statistics (lane i: LSE for i < kT, D
+    // otherwise); rows past N repeat row N - 1, which only invisible queries use
+    const int i = tid & (2 * kT - 1);
+    const int row = min(t * kT + (i & (kT - 1)), N - 1);
+    const float* src = i < kT ? lse_h : delta_h;
+    sstat = src[row] * (i < kT ? kLog2e : 1.f);
   }
   __device__ __forceinline__ void store(int b) {
 #pragma unroll
@@ -712,7 +714,9 @@ struct DkDv {
       *reinterpret_cast<uint4*>(qbuf(b) + st_off[i]) = sq[i];
       *reinterpret_cast<uint4*>(dbuf(b) + st_off[i]) = sd[i];
     }
-    if (tid < 2 * kT) stat[(b * 2 + tid / kT) * kT + (tid & (kT - 1))] = sstat;
+    // the four wavefronts store the same values: no branch
+    const int i = tid & (2 * kT - 1);
+    stat[(b * 2 + i / kT) * kT + (i & (kT - 1))] = sstat;
   }
   // LSE and D of half h of this lane's 16 queries (the queries 8 h .. 8 h + 7 of each
   // of its two runs of 8) of the tile in buffer b

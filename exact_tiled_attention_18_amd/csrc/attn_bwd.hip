@@ -23,12 +23,12 @@
 //              dO, LSE, D) of 32 rows through LDS.  Here S = Q K^T keeps one
 //              key per lane, with Q's and dO's rows permuted, so P and dS come
 //              out as B operands of dV^T += dO^T P and dK^T += Q^T dS.
-// Tiles are double-buffered: the next tile is loaded into registers while the
-// current one is used, then written to the other buffer before the step's
-// single barrier.  At d = 128 both the dQ and the dK/dV kernel are
-// software-pipelined instead (four tile buffers; each step interleaves the
-// score MFMAs of the next tile, the gradient MFMAs of the previous one and the
-// vector work of the current one); at d = 64 the plain kernels are kept.
+// The dQ kernel, and the dK/dV kernel at d = 128, are software-pipelined: four
+// tile buffers, and each step interleaves the score MFMAs of the next tile, the
+// gradient MFMAs of the previous one and the vector work of the current one.  At
+// d = 64 the dK/dV kernel is the plain loop, which fits two wavefronts per SIMD:
+// tiles double-buffered, the next one loaded into registers while the current
+// one is used, then written to the other buffer before the step's single barrier.
 //
 // A negative scale flips every sign bit of Q, a zero scale zeroes Q (the
 // kernels then use the positive multiplier |scale| * log2(e)): dQ = scale *
@@ -187,106 +187,6 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------- dQ
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) void bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                     const uint16_t* __restrict__ v,
-                                                     const uint16_t* __restrict__ dout,
-                                                     const float* __restrict__ lse, const float* __restrict__ delta,
-                                                     uint16_t* __restrict__ dq, int BH, int N, int nQB, float c,
-                                                     float dq_mul, uint32_t qxor, uint32_t qand) {
-  using T = Tile<D>;
-  constexpr int DK = D / 16, DB = D / 32, kBr = 256;
-  __shared__ __attribute__((aligned(16))) char smem[4 * T::BYTES];  // K and V, two buffers each
-  // K buffers at 0 and BYTES, V buffers at 2 * BYTES and 3 * BYTES
-  auto kbuf = [&](int b) { return smem + b * T::BYTES; };
-  auto vbuf = [&](int b) { return smem + (2 + b) * T::BYTES; };
-
-  const int L = blockIdx.x;
-  int qblk = CAUSAL ? (nQB - 1 - L / BH) : (L / BH);
-  int bh = L % BH;
-  if (!CAUSAL && BH % 8 == 0) grouped_item(L, BH, nQB, qblk, bh);
-  const size_t base = (size_t)bh * N * D;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, li = lane & 31;
-  const int q0 = qblk * kBr;
-  const int qi = q0 + (tid >> 6) * 32 + li;  // this lane's query
-
-  constexpr int kRsrcWord3 = 0x00020000;
-  const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(k + base), (short)0, N * D * 2, kRsrcWord3);
-  const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(v + base), (short)0, N * D * 2, kRsrcWord3);
-  const bool copier = tid < T::PIECES;
-  const int prow = (tid % T::PIECES) / (D / 8), pcol = (tid % (D / 8)) * 16;
-  const int ld_off = prow * D * 2 + pcol, st_off = piece_off<D>(prow, pcol / 16);
-  const RowRd krow = row_reader<D>(permuted_row(li), g);
-  const TrRd tr_off = tr_reader<D>(lane);
-
-  bf16x8 qf[DK], df[DK];
-#pragma unroll
-  for (int ks = 0; ks < DK; ++ks) {
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (qi < N) {
-      a = *reinterpret_cast<const uint4*>(q + base + (size_t)qi * D + ks * 16 + g * 8);
-      b = *reinterpret_cast<const uint4*>(dout + base + (size_t)qi * D + ks * 16 + g * 8);
-    }
-    a = make_uint4((a.x ^ qxor) & qand, (a.y ^ qxor) & qand, (a.z ^ qxor) & qand, (a.w ^ qxor) & qand);
-    qf[ks] = __builtin_bit_cast(bf16x8, a);
-    df[ks] = __builtin_bit_cast(bf16x8, b);
-  }
-  const float lse2 = qi < N ? lse[(size_t)bh * N + qi] * kLog2e : 0.f;
-  const float dd = qi < N ? delta[(size_t)bh * N + qi] : 0.f;
-  f32x16 acc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-
-  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
-  const int nT = (kv_end + kT - 1) / kT;
-  uint4 sk = make_uint4(0, 0, 0, 0), sv = sk;
-  if (copier) {
-    sk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, ld_off, 0, 0));
-    sv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, ld_off, 0, 0));
-    *reinterpret_cast<uint4*>(kbuf(0) + st_off) = sk;
-    *reinterpret_cast<uint4*>(vbuf(0) + st_off) = sv;
-  }
-  __syncthreads();
-  for (int t = 0; t < nT; ++t) {
-    const int cur = t & 1;
-    if (copier && t + 1 < nT) {
-      sk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, ld_off + (t + 1) * kT * D * 2, 0, 0));
-      sv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, ld_off + (t + 1) * kT * D * 2, 0, 0));
-    }
-    // S^T = K Q'^T and dP^T = V dO^T, one query per lane
-    f32x16 st = {}, dpt = {};
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-      st = mfma(read_row<D>(kbuf(cur), krow, ks), qf[ks], st);
-      dpt = mfma(read_row<D>(vbuf(cur), krow, ks), df[ks], dpt);
-    }
-    // dS^T = P^T * (dP^T - D), keys masked where not visible
-    float ds[16];
-    const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - t * kT;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = row_of_reg(r, g) <= lim ? exp2_fast(fmaf(st[r], c, -lse2)) : 0.f;
-      ds[r] = p * (dpt[r] - dd);
-    }
-    const bf16x8 db0 = pack8(ds), db1 = pack8(ds + 8);
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      acc[db] = mfma(read_tr<D>(kbuf(cur), tr_off, db, 0), db0, acc[db]);
-      acc[db] = mfma(read_tr<D>(kbuf(cur), tr_off, db, 1), db1, acc[db]);
-    }
-    if (copier && t + 1 < nT) {
-      *reinterpret_cast<uint4*>(kbuf(cur ^ 1) + st_off) = sk;
-      *reinterpret_cast<uint4*>(vbuf(cur ^ 1) + st_off) = sv;
-    }
-    __syncthreads();
-  }
-  if (qi < N) store_rows<D>(dq + base + (size_t)qi * D, acc, dq_mul, g);
-}
-
-// ---------------------------------------------------------------- dQ (d = 128)
 // Software pipeline over key tiles, as in the dK/dV kernel: step t issues the MFMAs
 // of S^T_{t+1} = K_{t+1} Q'^T and dP^T_{t+1} = V_{t+1} dO^T, the MFMAs of
 // dQ^T += K_{t-1}^T dS^T_{t-1}, and the vector work that turns S^T_t, dP^T_t into
@@ -586,10 +486,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       sq[i] = make_uint4((a.x ^ qxor) & qand, (a.y ^ qxor) & qand, (a.z ^ qxor) & qand, (a.w ^ qxor) & qand);
       sd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, ld_off[i] + t * kT * D * 2, 0, 0));
     }
-    if (tid < 2 * kT) {
-      const int row = t * kT + (tid & (kT - 1));
-      sstat = row < N ? (tid < kT ? lse[(size_t)bh * N + row] * kLog2e : delta[(size_t)bh * N + row]) : 0.f;
-    }
+    // every wavefront loads the tile's 2 kT statistics (lane i: LSE for i < kT, D
+    // otherwise); rows past N repeat row N - 1, which only invisible queries use
+    const int i = tid & (2 * kT - 1);
+    const int row = min(t * kT + (i & (kT - 1)), N - 1);
+    const float* src = (i < kT ? lse : delta) + (size_t)bh * N;
+    sstat = src[row] * (i < kT ? kLog2e : 1.f);
   };
   auto store = [&](int b) {
 #pragma unroll
@@ -597,7 +499,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       *reinterpret_cast<uint4*>(qbuf(b) + st_off[i]) = sq[i];
       *reinterpret_cast<uint4*>(dbuf(b) + st_off[i]) = sd[i];
     }
-    if (tid < 2 * kT) stat[b][tid / kT][tid & (kT - 1)] = sstat;
+    const int i = tid & (2 * kT - 1);  // the four wavefronts store the same values
+    stat[b][i / kT][i & (kT - 1)] = sstat;
   };
   if (t0 < nQT) {
     load(t0);
@@ -632,12 +535,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
       }
     }
     float p[16], ds[16];
+    // a tile below N that lies wholly after every key of a block below N sees all of them
+    const bool full = (t + 1) * kT <= N && k0 + kBk <= N && (!CAUSAL || k0 + kBk <= t * kT + 1);
+    if (full) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = t * kT + row_of_reg(r, g);
-      const bool vis = qr < N && kj < N && (!CAUSAL || kj <= qr);
-      p[r] = vis ? exp2_fast(fmaf(s[r], c, -ls[r])) : 0.f;
-      ds[r] = p[r] * (dp[r] - dl[r]);
+      for (int r = 0; r < 16; ++r) {
+        p[r] = exp2_fast(fmaf(s[r], c, -ls[r]));
+        ds[r] = p[r] * (dp[r] - dl[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = t * kT + row_of_reg(r, g);
+        const bool vis = qr < N && kj < N && (!CAUSAL || kj <= qr);
+        p[r] = vis ? exp2_fast(fmaf(s[r], c, -ls[r])) : 0.f;
+        ds[r] = p[r] * (dp[r] - dl[r]);
+      }
     }
     const bf16x8 pb0 = pack8(p), pb1 = pack8(p + 8), sb0 = pack8(ds), sb1 = pack8(ds + 8);
     // dV^T += dO^T P and dK^T += Q'^T dS
@@ -984,15 +897,12 @@ hipError_t launch_d(const BwdArgs& a) {
   const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
   const int nQB = (N + 255) / 256;
-  if constexpr (D == 128)
-    hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v,
-                       dout, a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v, dout,
-                       a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v,
+                     dout, a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
   const int nKB = (N + 127) / 128;
   // d = 128: the pipelined kernel (one wavefront per SIMD either way); d = 64: the
-  // plain one, which fits two wavefronts per SIMD and hides its latencies with the second
+  // plain one, which fits two wavefronts per SIMD and hides its latencies with the
+  // second (the pipelined one would need more than the 256 registers that allows)
   if constexpr (D == 128)
     hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(256), 0, a.stream, q, k,
                        v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N,

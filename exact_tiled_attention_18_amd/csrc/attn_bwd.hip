@@ -570,50 +570,67 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
   }
 }
 
-// ---------------------------------------------------------------- dK, dV (d = 128)
-// Software pipeline over query tiles: step t issues the MFMAs of S_{t+1} = Q_{t+1} K^T
-// and dP_{t+1} = dO_{t+1} V^T, the MFMAs of dV += dO_{t-1}^T P_{t-1} and
-// dK += Q_{t-1}^T dS_{t-1}, and the vector work that turns S_t, dP_t into P_t, dS_t;
-// none depends on another, so they are interleaved chunk by chunk.  Four LDS
-// buffers hold tiles t-1 .. t+2 (tile t waits there for its dV/dK products in the
-// next step); tile t+2 is written from registers loaded one step earlier.
+// ---------------------------------------------------------------- dK, dV (d = 128): wavefront pairs
+// Eight wavefronts, two per SIMD.  Wavefront w < 4 (the P side) and wavefront w + 4 (the
+// dS side) share the 32 keys 32 w .. 32 w + 31 of the block.  The P side holds K and dV:
+// it computes S = Q K^T, turns S into P and accumulates dV^T += dO^T P.  The dS side holds
+// V and dK: it computes dP = dO V^T, takes P from the P side through LDS (in fp32, so dS is
+// formed from exactly the values the P side rounded for dV), forms dS = P (dP - D) and
+// accumulates dK^T += Q^T dS.  Each side keeps about half the state of one wavefront doing
+// both, so each fits the 256 registers that two wavefronts per SIMD allow, and every SIMD
+// runs one wavefront of each side, whose MFMAs and vector work overlap.  Step t:
+//   P side:  MFMAs of S_{t+1} = Q_{t+1} K^T and dV += dO_{t-1}^T P_{t-1}; vector work
+//            P_t from S_t, written to LDS;
+//   dS side: MFMAs of dP_t = dO_t V^T and dK += Q_{t-2}^T dS_{t-2}; vector work dS_{t-1}
+//            from P_{t-1} (written in step t-1) and dP_{t-1}.
+// Six LDS buffers hold tiles t-2 .. t+3 (tile t+2 is written in step t); the steps run two
+// past the last tile to finish the products, on tiles past N, which load as zeros.
 template <int D, bool CAUSAL>
-struct DkDv {
+struct DkDvPair {
   using T = Tile<D>;
-  static constexpr int DK = D / 16, DB = D / 32, NB = 4;
-  static constexpr int kPer = T::PIECES / 256;  // 16-byte pieces per thread and operand tile (1 or 2)
-  static constexpr int EPC = 16 / DK;           // score elements per chunk (2 or 4)
-  static_assert(DK == 2 * DB, "one dV/dK operand pair per chunk");
+  static constexpr int DK = D / 16, DB = D / 32, NB = 6;
+  static constexpr int EPC = 16 / DK;  // score elements per chunk
+  static_assert(DK == 8 && EPC == 2, "written for d = 128");
+  static_assert(T::PIECES == 512, "one 16-byte piece per thread and operand tile");
 
-  bf16x8 kf[DK], vf[DK];
-  f32x16 dva[DB], dka[DB];
-  f32x16 s[2], dp[2];        // S and dP of tiles t (parity B) and t+1
-  uint32_t pw[2][8], sw[2][8];  // P and dS (bf16 pairs) of tiles t (parity B) and t-1
-  bf16x8 opq[2], opd[2], opv[2], opk[2];  // operands of the next chunk
-  uint4 sq[kPer], sd[kPer];
-  float sstat;
-  float ls[16], dl[16];
-
+  // both sides
   char* smem;
-  float* stat;  // [NB][2][kT]
+  float* stat;  // [NB][2][kT]: LSE * log2(e), D
+  float4* xp;   // [4 key groups][2 parities][4][64 lanes]: P of one tile, fp32
   __amdgpu_buffer_rsrc_t qrs, drs;
   const float* lse_h;
   const float* delta_h;
-  int N, tid, g, li, kj;
+  int N, tid, g, li, kj, kg, lane;
   RowRd qrow;
   TrRd tr_off;
-  int ld_off[kPer], st_off[kPer];
+  int ld_off, st_off;
+  uint4 sq, sd;
+  float sstat;
   float c;  // scale * log2(e), signed: Q enters unchanged
+  // P side
+  bf16x8 kf[DK];
+  f32x16 dva[DB];
+  f32x16 s[2];          // S of tiles t (parity B) and t+1
+  uint32_t pw[2][8];    // P (bf16 pairs) of tiles t (parity B) and t-1
+  bf16x8 opq[2], opv[2];
+  float ls[16];
+  float4 pout;          // four P values on their way to LDS
+  // dS side
+  bf16x8 vf[DK];
+  f32x16 dka[DB];
+  f32x16 dp[2];         // dP of tiles t (parity B) and t-1
+  uint32_t sw[2][8];    // dS (bf16 pairs) of tiles t-1 (parity B) and t-2
+  bf16x8 opd[2], opk[2];
+  float dl[16];
+  float4 pin[4];        // P of tile t-1, from LDS
 
   __device__ __forceinline__ char* qbuf(int b) const { return smem + b * T::BYTES; }
   __device__ __forceinline__ char* dbuf(int b) const { return smem + (NB + b) * T::BYTES; }
+  __device__ __forceinline__ float4* xslot(int par, int i) const { return xp + ((kg * 2 + par) * 4 + i) * 64 + lane; }
 
   __device__ __forceinline__ void load(int t) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      sq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ld_off[i] + t * kT * D * 2, 0, 0));
-      sd[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, ld_off[i] + t * kT * D * 2, 0, 0));
-    }
+    sq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(qrs, ld_off + t * kT * D * 2, 0, 0));
+    sd = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, ld_off + t * kT * D * 2, 0, 0));
     // every wavefront loads the tile's 2 kT statistics (lane i: LSE for i < kT, D
     // otherwise); rows past N repeat row N - 1, which only invisible queries use
     const int i = tid & (2 * kT - 1);
@@ -622,154 +639,184 @@ struct DkDv {
     sstat = src[row] * (i < kT ? kLog2e : 1.f);
   }
   __device__ __forceinline__ void store(int b) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      *reinterpret_cast<uint4*>(qbuf(b) + st_off[i]) = sq[i];
-      *reinterpret_cast<uint4*>(dbuf(b) + st_off[i]) = sd[i];
-    }
-    // the four wavefronts store the same values: no branch
-    const int i = tid & (2 * kT - 1);
+    *reinterpret_cast<uint4*>(qbuf(b) + st_off) = sq;
+    *reinterpret_cast<uint4*>(dbuf(b) + st_off) = sd;
+    const int i = tid & (2 * kT - 1);  // the eight wavefronts store the same values
     stat[(b * 2 + i / kT) * kT + (i & (kT - 1))] = sstat;
   }
-  // LSE and D of half h of this lane's 16 queries (the queries 8 h .. 8 h + 7 of each
-  // of its two runs of 8) of the tile in buffer b
-  __device__ __forceinline__ void read_stats_half(int b, int h) {
-    const float4* sl = reinterpret_cast<const float4*>(stat + (b * 2) * kT);
-    const float4* sdl = reinterpret_cast<const float4*>(stat + (b * 2 + 1) * kT);
+  // statistic st (0: LSE, 1: D) of half h of this lane's 16 queries (the queries
+  // 8 h .. 8 h + 7 of each of its two runs of 8) of the tile in buffer b
+  __device__ __forceinline__ void read_stat_half(float (&dst)[16], int b, int st, int h) const {
+    const float4* sl = reinterpret_cast<const float4*>(stat + (b * 2 + st) * kT);
     const float4 a0 = sl[4 * h + 2 * g], a1 = sl[4 * h + 2 * g + 1];
-    const float4 b0 = sdl[4 * h + 2 * g], b1 = sdl[4 * h + 2 * g + 1];
     const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      ls[8 * h + r] = av[r];
-      dl[8 * h + r] = bv[r];
-    }
-  }
-  // LSE and D of this lane's 16 queries (two runs of 8) of the tile in buffer b
-  __device__ __forceinline__ void read_stats(int b) {
-    const float4* sl = reinterpret_cast<const float4*>(stat + (b * 2) * kT);
-    const float4* sdl = reinterpret_cast<const float4*>(stat + (b * 2 + 1) * kT);
-    const float4 a0 = sl[2 * g], a1 = sl[2 * g + 1], a2 = sl[4 + 2 * g], a3 = sl[5 + 2 * g];
-    const float4 b0 = sdl[2 * g], b1 = sdl[2 * g + 1], b2 = sdl[4 + 2 * g], b3 = sdl[5 + 2 * g];
-    const float av[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w, a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-    const float bv[16] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w, b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ls[r] = av[r];
-      dl[r] = bv[r];
-    }
-  }
-  // P and dS of score elements [e0, e0 + EPC) of tile t (parity B); without G every
-  // query of the tile is below N and sees every key of the block
-  template <int B, bool G>
-  __device__ __forceinline__ void grad_slice(int t, int e0) {
-#pragma unroll
-    for (int e = e0; e < e0 + EPC; e += 2) {
-      float p2[2], d2[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = e + h;
-        const int qr = t * kT + row_of_reg(r, g);
-        const bool vis = !G || (qr < N && kj < N && (!CAUSAL || kj <= qr));
-        // An empty volatile asm on the scores, still in the accumulation registers:
-        // the copies out of them and the vector work after it stay in this chunk
-        // (the scheduler otherwise gathers all 32 copies, or all 16 exponentials, into
-        // one chunk, where they hold up that chunk's MFMAs).
-        float sv = s[B][r], dv = dp[B][r];
-        asm volatile("" : "+a"(sv), "+a"(dv));
-        p2[h] = vis ? exp2_fast(fmaf(sv, c, -ls[r])) : 0.f;
-        d2[h] = p2[h] * (dv - dl[r]);
-      }
-      pw[B][e >> 1] = pack_bf16x2(p2[0], p2[1]);
-      sw[B][e >> 1] = pack_bf16x2(d2[0], d2[1]);
-      // and a use of the packed results here, so that the compiler does not sink the
-      // work towards its uses in the next step
-      asm volatile("" ::"v"(pw[B][e >> 1]), "v"(sw[B][e >> 1]));
-    }
+    for (int r = 0; r < 8; ++r) dst[8 * h + r] = av[r];
   }
   __device__ __forceinline__ bf16x8 word8(const uint32_t (&w)[8], int mm) const {
     return __builtin_bit_cast(bf16x8, make_uint4(w[4 * mm], w[4 * mm + 1], w[4 * mm + 2], w[4 * mm + 3]));
   }
-  // operands of chunk ch: S/dP operands of the tile in buffer bn, dV/dK operands of buffer bo
-  __device__ __forceinline__ void read_sdp(int slot, int ch, int bn) {
-    opq[slot] = read_row<D>(qbuf(bn), qrow, ch);
-    opd[slot] = read_row<D>(dbuf(bn), qrow, ch);
-  }
-  __device__ __forceinline__ void read_grad(int slot, int ch, int bo) {
-    opv[slot] = read_tr<D>(dbuf(bo), tr_off, ch % DB, ch / DB);
-    opk[slot] = read_tr<D>(qbuf(bo), tr_off, ch % DB, ch / DB);
+  __device__ __forceinline__ void chunk_schedule() const {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);  // DS writes
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // VMEM reads
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // one step for tile t in buffer cur (parity B = (t - t0) & 1); the dV/dK operands
-  // of its chunk 0 and the statistics of tile t were read by the previous step (tile
-  // t+1's were written before the last barrier only, so its S/dP operands are read
-  // here, and its statistics from the middle of the step on, into the registers of
-  // the elements already done).  Tile t+3 is loaded whether or not it exists: past
-  // the last tile the buffer range check returns zeros, which no step uses.
-  template <int B, bool G = true>
-  __device__ __forceinline__ void step(int t, int cur) {
+  // ---- P side, step t (tile t in buffer cur, parity B = (t - t0) & 1); the dV operand
+  // of chunk 0 was read by the previous step, S_{t+1}'s after the barrier
+  template <int B, bool G>
+  __device__ __forceinline__ void step_p(int t, int cur) {
     const int bn = (cur + 1) % NB, bo = (cur + NB - 1) % NB, bw = (cur + 2) % NB;
-    read_sdp(0, 0, bn);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[B ^ 1][r] = dp[B ^ 1][r] = 0.f;
+    opq[0] = read_row<D>(qbuf(bn), qrow, 0);
 #pragma unroll
     for (int ch = 0; ch < DK; ++ch) {
       if (ch + 1 < DK) {
-        read_sdp((ch + 1) & 1, ch + 1, bn);
-        read_grad((ch + 1) & 1, ch + 1, bo);
+        opq[(ch + 1) & 1] = read_row<D>(qbuf(bn), qrow, ch + 1);
+        opv[(ch + 1) & 1] = read_tr<D>(dbuf(bo), tr_off, (ch + 1) % DB, (ch + 1) / DB);
       } else {
-        read_grad(0, 0, cur);  // the next step's chunk 0: dV/dK operands of tile t
+        opv[0] = read_tr<D>(dbuf(cur), tr_off, 0, 0);  // the next step's chunk 0: dO^T of tile t
       }
       const int sl = ch & 1, db = ch % DB, mm = ch / DB;
       dva[db] = mfma(opv[sl], word8(pw[B ^ 1], mm), dva[db]);
-      s[B ^ 1] = mfma(opq[sl], kf[ch], s[B ^ 1]);
-      dka[db] = mfma(opk[sl], word8(sw[B ^ 1], mm), dka[db]);
-      dp[B ^ 1] = mfma(opd[sl], vf[ch], dp[B ^ 1]);
-      grad_slice<B, G>(t, ch * EPC);
-      // the next tile's statistics, into the halves this step has finished with
-      if (ch == DK / 2) read_stats_half(bn, 0);
-      if (ch == DK - 1) read_stats_half(bn, 1);
+      s[B ^ 1] = mfma(opq[sl], kf[ch], ch == 0 ? f32x16{} : s[B ^ 1]);
+      // P of score elements 2 ch, 2 ch + 1 of tile t
+      float p2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 2 * ch + h;
+        const int qr = t * kT + row_of_reg(r, g);
+        const bool vis = !G || (qr < N && kj < N && (!CAUSAL || kj <= qr));
+        float sv = s[B][r];
+        asm volatile("" : "+v"(sv));  // keeps this element's work in its chunk
+        p2[h] = vis ? exp2_fast(fmaf(sv, c, -ls[r])) : 0.f;
+      }
+      pw[B][ch] = pack_bf16x2(p2[0], p2[1]);
+      if (ch & 1) {
+        pout.z = p2[0];
+        pout.w = p2[1];
+        *xslot(B, ch >> 1) = pout;
+      } else {
+        pout.x = p2[0];
+        pout.y = p2[1];
+      }
+      asm volatile("" ::"v"(pw[B][ch]));  // a use in this chunk: no sinking into the next step
+      // the next tile's LSE, into the halves this step has finished with
+      if (ch == DK / 2) read_stat_half(ls, bn, 0, 0);
+      if (ch == DK - 1) read_stat_half(ls, bn, 0, 1);
       if (ch == 1) store(bw);
       if (ch == 2) load(t + 3);
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 100, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);  // DS writes
-      __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);  // VMEM reads
-      __builtin_amdgcn_sched_barrier(0);
+      chunk_schedule();
     }
     __syncthreads();
   }
-  // dV/dK products of the last tile (parity B, buffer b); operands of chunk 0 read
+
+  // ---- dS side, step t: dP_t from the tile in buffer cur, dS_{t-1} (tile in cur - 1),
+  // dK products with dS_{t-2} (tile in cur - 2); chunk 0's operands were read by the
+  // previous step (all these tiles were in LDS before its barrier)
   template <int B>
-  __device__ __forceinline__ void last(int b) {
+  __device__ __forceinline__ void step_d(int t, int cur) {
+    const int bn = (cur + 1) % NB, bo = (cur + NB - 1) % NB, bo2 = (cur + NB - 2) % NB, bw = (cur + 2) % NB;
+    pin[0] = *xslot(B ^ 1, 0);
 #pragma unroll
     for (int ch = 0; ch < DK; ++ch) {
-      const int db = ch % DB, mm = ch / DB;
-      const bf16x8 av = ch == 0 ? opv[0] : read_tr<D>(dbuf(b), tr_off, db, mm);
-      const bf16x8 ak = ch == 0 ? opk[0] : read_tr<D>(qbuf(b), tr_off, db, mm);
-      dva[db] = mfma(av, word8(pw[B], mm), dva[db]);
-      dka[db] = mfma(ak, word8(sw[B], mm), dka[db]);
+      if (ch + 1 < DK) {
+        opd[(ch + 1) & 1] = read_row<D>(dbuf(cur), qrow, ch + 1);
+        opk[(ch + 1) & 1] = read_tr<D>(qbuf(bo2), tr_off, (ch + 1) % DB, (ch + 1) / DB);
+      } else {
+        opd[0] = read_row<D>(dbuf(bn), qrow, 0);         // the next step's chunk 0: dO of tile t+1
+        opk[0] = read_tr<D>(qbuf(bo), tr_off, 0, 0);     // and Q^T of tile t-1
+      }
+      if ((ch & 1) && ch + 1 < DK) pin[(ch + 1) >> 1] = *xslot(B ^ 1, (ch + 1) >> 1);
+      const int sl = ch & 1, db = ch % DB, mm = ch / DB;
+      dka[db] = mfma(opk[sl], word8(sw[B ^ 1], mm), dka[db]);
+      dp[B] = mfma(opd[sl], vf[ch], ch == 0 ? f32x16{} : dp[B]);
+      // dS of score elements 2 ch, 2 ch + 1 of tile t-1
+      float d2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 2 * ch + h;
+        float dv = dp[B ^ 1][r];
+        asm volatile("" : "+v"(dv));
+        const float4 pq = pin[r >> 2];
+        const float p = (r & 3) == 0 ? pq.x : (r & 3) == 1 ? pq.y : (r & 3) == 2 ? pq.z : pq.w;
+        d2[h] = p * (dv - dl[r]);
+      }
+      sw[B][ch] = pack_bf16x2(d2[0], d2[1]);
+      asm volatile("" ::"v"(sw[B][ch]));
+      // D of tile t, for the next step
+      if (ch == DK / 2) read_stat_half(dl, cur, 1, 0);
+      if (ch == DK - 1) read_stat_half(dl, cur, 1, 1);
+      if (ch == 1) store(bw);
+      if (ch == 2) load(t + 3);
+      chunk_schedule();
+    }
+    __syncthreads();
+  }
+
+  // all steps of one side: tiles t0 .. nQT - 1 and two more; the P side's steps on
+  // tiles [t0 + 4, tf) (causal; [0, tf) otherwise) skip the visibility test
+  template <bool PSIDE>
+  __device__ __forceinline__ void run(int t0, int nQT, int tf) {
+    const int tend = nQT + 2;
+    int t = t0;
+    auto six = [&](auto guard) {
+      constexpr bool G = decltype(guard)::value;
+      if constexpr (PSIDE) {
+        step_p<0, G>(t, 0);
+        step_p<1, G>(t + 1, 1);
+        step_p<0, G>(t + 2, 2);
+        step_p<1, G>(t + 3, 3);
+        step_p<0, G>(t + 4, 4);
+        step_p<1, G>(t + 5, 5);
+      } else {
+        step_d<0>(t, 0);
+        step_d<1>(t + 1, 1);
+        step_d<0>(t + 2, 2);
+        step_d<1>(t + 3, 3);
+        step_d<0>(t + 4, 4);
+        step_d<1>(t + 5, 5);
+      }
+    };
+    if (CAUSAL && t + 6 <= tend) {
+      six(std::true_type{});
+      t += 6;
+    }
+    for (; t + 6 <= tf; t += 6) six(std::false_type{});
+    for (; t + 6 <= tend; t += 6) six(std::true_type{});
+    for (; t + 2 <= tend; t += 2) {
+      if constexpr (PSIDE) {
+        step_p<0, true>(t, (t - t0) % NB);
+        step_p<1, true>(t + 1, (t + 1 - t0) % NB);
+      } else {
+        step_d<0>(t, (t - t0) % NB);
+        step_d<1>(t + 1, (t + 1 - t0) % NB);
+      }
+    }
+    if (t < tend) {
+      if constexpr (PSIDE)
+        step_p<0, true>(t, (t - t0) % NB);
+      else
+        step_d<0>(t, (t - t0) % NB);
     }
   }
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
+__global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int BH, int N, float c, float dk_mul) {
-  using W = DkDv<D, CAUSAL>;
+  using W = DkDvPair<D, CAUSAL>;
   using T = Tile<D>;
-  constexpr int DK = W::DK, DB = W::DB, NB = W::NB, kPer = W::kPer, kBk = 128;
+  constexpr int DK = W::DK, DB = W::DB, NB = W::NB, kBk = 128;
   __shared__ __attribute__((aligned(16))) char smem[2 * NB * T::BYTES];  // Q' buffers, then dO buffers
-  __shared__ __attribute__((aligned(16))) float stat[NB * 2 * kT];       // [buffer][LSE*log2e, D][row]
+  __shared__ __attribute__((aligned(16))) float stat[NB * 2 * kT];
+  __shared__ __attribute__((aligned(16))) float4 xp[4 * 2 * 4 * 64];
 
   W w;
   const int L = blockIdx.x;
@@ -778,15 +825,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
   if (!CAUSAL && BH % 8 == 0) grouped_item(L, BH, (int)(gridDim.x / BH), kblk, bh);
   const size_t base = (size_t)bh * N * D;
   w.tid = threadIdx.x;
-  const int lane = w.tid & 63;
-  w.g = lane >> 5;
-  w.li = lane & 31;
+  w.lane = w.tid & 63;
+  w.g = w.lane >> 5;
+  w.li = w.lane & 31;
+  w.kg = (w.tid >> 6) & 3;
+  const bool pside = w.tid < 256;
   const int k0 = kblk * kBk;
-  w.kj = k0 + (w.tid >> 6) * 32 + w.li;  // this lane's key
+  w.kj = k0 + w.kg * 32 + w.li;  // this lane's key
   w.N = N;
   w.c = c;
   w.smem = smem;
   w.stat = stat;
+  w.xp = xp;
   w.lse_h = lse + (size_t)bh * N;
   w.delta_h = delta + (size_t)bh * N;
   constexpr int kRsrcWord3 = 0x00020000;
@@ -794,91 +844,75 @@ __global__ __launch_bounds__(256) void bwd_dkdv_pipe_kernel(
   // even where Q K^T would overflow, as in the forward, which zeroes Q
   w.qrs = __builtin_amdgcn_make_buffer_rsrc((void*)(q + base), (short)0, c == 0.f ? 0 : N * D * 2, kRsrcWord3);
   w.drs = __builtin_amdgcn_make_buffer_rsrc((void*)(dout + base), (short)0, N * D * 2, kRsrcWord3);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int piece = w.tid + 256 * i;
-    const int prow = piece / (D / 8), pcol = (piece % (D / 8)) * 16;
-    w.ld_off[i] = prow * D * 2 + pcol;
-    w.st_off[i] = piece_off<D>(prow, pcol / 16);
+  {
+    const int prow = w.tid / (D / 8), pcol = (w.tid % (D / 8)) * 16;
+    w.ld_off = prow * D * 2 + pcol;
+    w.st_off = piece_off<D>(prow, pcol / 16);
   }
   w.qrow = row_reader<D>(permuted_row(w.li), w.g);
-  w.tr_off = tr_reader<D>(lane);
+  w.tr_off = tr_reader<D>(w.lane);
 
+  // the side's operand rows of the block: K (P side) or V (dS side)
+  {
+    const uint16_t* src = pside ? k : v;
 #pragma unroll
-  for (int ks = 0; ks < DK; ++ks) {
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
-    if (w.kj < N) {
-      a = *reinterpret_cast<const uint4*>(k + base + (size_t)w.kj * D + ks * 16 + w.g * 8);
-      b = *reinterpret_cast<const uint4*>(v + base + (size_t)w.kj * D + ks * 16 + w.g * 8);
+    for (int ks = 0; ks < DK; ++ks) {
+      uint4 a = make_uint4(0, 0, 0, 0);
+      if (w.kj < N) a = *reinterpret_cast<const uint4*>(src + base + (size_t)w.kj * D + ks * 16 + w.g * 8);
+      if (pside)
+        w.kf[ks] = __builtin_bit_cast(bf16x8, a);
+      else
+        w.vf[ks] = __builtin_bit_cast(bf16x8, a);
     }
-    w.kf[ks] = __builtin_bit_cast(bf16x8, a);
-    w.vf[ks] = __builtin_bit_cast(bf16x8, b);
   }
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) w.dva[db][r] = w.dka[db][r] = 0.f;
-
-  // query tiles that see any key of the block
   const int t0 = CAUSAL ? k0 / kT : 0;
   const int nQT = (N + kT - 1) / kT;
   if (t0 < nQT) {
-    // prologue: tiles t0 and t0+1 into buffers 0 and 1, buffer 3 (tile t0-1 of the
-    // first step's dV/dK products) zeroed along with P_{t0-1} and dS_{t0-1}; S_t0, dP_t0
+    // prologue: tiles t0 and t0+1 into buffers 0 and 1; buffers 4 and 5 (tiles t0-2 and
+    // t0-1 of the first steps' products) zeroed with their statistics, and the P slot of
+    // tile t0-1; tile t0+2 loaded for the first step
     w.load(t0);
     w.store(0);
     w.load(t0 + 1);
     w.store(1);
-    for (int i = w.tid; i < T::BYTES / 16; i += 256) {
-      *reinterpret_cast<uint4*>(w.qbuf(3) + 16 * i) = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(w.dbuf(3) + 16 * i) = make_uint4(0, 0, 0, 0);
+    for (int i = w.tid; i < 2 * T::BYTES / 16; i += 512) {
+      *reinterpret_cast<uint4*>(w.qbuf(4) + 16 * i) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(w.dbuf(4) + 16 * i) = make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w.pw[1][i] = w.sw[1][i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) w.s[0][r] = w.dp[0][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-      w.s[0] = mfma(read_row<D>(w.qbuf(0), w.qrow, ks), w.kf[ks], w.s[0]);
-      w.dp[0] = mfma(read_row<D>(w.dbuf(0), w.qrow, ks), w.vf[ks], w.dp[0]);
-    }
+    for (int i = w.tid; i < 2 * 2 * kT; i += 512) stat[4 * 2 * kT + i] = 0.f;
+    for (int i = w.tid; i < 4 * 4 * 64; i += 512) xp[((i >> 8) * 2 + 1) * 256 + (i & 255)] = make_float4(0.f, 0.f, 0.f, 0.f);
     w.load(t0 + 2);
-    w.read_grad(0, 0, 3);
-    w.read_stats(0);
-    int t = t0;
-    // four steps per iteration (two parities times the four buffers): buffer indices
-    // are constants, so LDS addresses fold into instruction offsets.  Query tiles
-    // [t0 + 4, tf) (causal; [0, tf) otherwise) lie wholly below N and after every key of
-    // a block that ends at or before N: they skip the per-element visibility test.
-    const int tf = k0 + kBk <= N ? N / kT : 0;
-    auto quad = [&](auto guard) {
-      constexpr bool G = decltype(guard)::value;
-      w.template step<0, G>(t, 0);
-      w.template step<1, G>(t + 1, 1);
-      w.template step<0, G>(t + 2, 2);
-      w.template step<1, G>(t + 3, 3);
-    };
-    if (CAUSAL && t + 3 < nQT) {
-      quad(std::true_type{});
-      t += 4;
-    }
-    for (; t + 3 < tf; t += 4) quad(std::false_type{});
-    for (; t + 3 < nQT; t += 4) quad(std::true_type{});
-    for (; t + 1 < nQT; t += 2) {
-      w.template step<0>(t, (t - t0) % NB);
-      w.template step<1>(t + 1, (t + 1 - t0) % NB);
-    }
-    if (t < nQT) {
-      w.template step<0>(t, (t - t0) % NB);
-      w.template last<0>((t - t0) % NB);
+    __syncthreads();
+    if (pside) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w.dva[db][r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w.pw[1][i] = 0u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) w.read_stat_half(w.ls, 0, 0, h);
+      w.s[0] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) w.s[0] = mfma(read_row<D>(w.qbuf(0), w.qrow, ks), w.kf[ks], w.s[0]);
+      w.opv[0] = read_tr<D>(w.dbuf(5), w.tr_off, 0, 0);
+      w.template run<true>(t0, nQT, k0 + kBk <= N ? N / kT : 0);
+      if (w.kj < N) store_rows<D>(dv + base + (size_t)w.kj * D, w.dva, 1.f, w.g);
     } else {
-      w.template last<1>((t - 1 - t0) % NB);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w.dka[db][r] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w.sw[1][i] = 0u;
+      w.dp[1] = f32x16{};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) w.read_stat_half(w.dl, 5, 1, h);
+      w.opd[0] = read_row<D>(w.dbuf(0), w.qrow, 0);
+      w.opk[0] = read_tr<D>(w.qbuf(4), w.tr_off, 0, 0);
+      w.template run<false>(t0, nQT, 0);
+      if (w.kj < N) store_rows<D>(dk + base + (size_t)w.kj * D, w.dka, dk_mul, w.g);
     }
-  }
-  if (w.kj < N) {
-    store_rows<D>(dv + base + (size_t)w.kj * D, w.dva, 1.f, w.g);
-    store_rows<D>(dk + base + (size_t)w.kj * D, w.dka, dk_mul, w.g);
   }
 }
 
@@ -904,7 +938,7 @@ hipError_t launch_d(const BwdArgs& a) {
   // plain one, which fits two wavefronts per SIMD and hides its latencies with the
   // second (the pipelined one would need more than the 256 registers that allows)
   if constexpr (D == 128)
-    hipLaunchKernelGGL((bwd_dkdv_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(256), 0, a.stream, q, k,
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(512), 0, a.stream, q, k,
                        v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N,
                        a.scale * kLog2e, a.scale);
   else

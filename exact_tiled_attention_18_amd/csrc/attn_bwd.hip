@@ -583,8 +583,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 //            P_t from S_t, written to LDS;
 //   dS side: MFMAs of dP_t = dO_t V^T and dK += Q_{t-2}^T dS_{t-2}; vector work dS_{t-1}
 //            from P_{t-1} (written in step t-1) and dP_{t-1}.
-// Six LDS buffers hold tiles t-2 .. t+3 (tile t+2 is written in step t); the steps run two
-// past the last tile to finish the products, on tiles past N, which load as zeros.
+// Six LDS buffers hold tiles t-2 .. t+3 (tile t+2 is written in step t).  After the last
+// step each side finishes the products it still owes (dV of the last tile; dS of the last
+// tile and dK of the last two), without further barriers.
 template <int D, bool CAUSAL>
 struct DkDvPair {
   using T = Tile<D>;
@@ -758,11 +759,54 @@ struct DkDvPair {
     __syncthreads();
   }
 
-  // all steps of one side: tiles t0 .. nQT - 1 and two more; the P side's steps on
+  // ---- after the last step (parity B, tile in buffer cur): the products still owed,
+  // with no barrier (they read only tiles already in LDS and the P slot of the last tile)
+  template <int B>
+  __device__ __forceinline__ void tail_p(int cur) {
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {  // dV += dO^T P of the last tile
+      const int db = ch % DB, mm = ch / DB;
+      const bf16x8 av = ch == 0 ? opv[0] : read_tr<D>(dbuf(cur), tr_off, db, mm);
+      dva[db] = mfma(av, word8(pw[B], mm), dva[db]);
+    }
+  }
+  template <int B>
+  __device__ __forceinline__ void tail_d(int cur) {
+    const int bo = (cur + NB - 1) % NB;
+    // dS of the last tile, into the free dS buffer
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pin[i] = *xslot(B, i);
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {
+      float d2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 2 * ch + h;
+        const float4 pq = pin[r >> 2];
+        const float p = (r & 3) == 0 ? pq.x : (r & 3) == 1 ? pq.y : (r & 3) == 2 ? pq.z : pq.w;
+        d2[h] = p * (dp[B][r] - dl[r]);
+      }
+      sw[B ^ 1][ch] = pack_bf16x2(d2[0], d2[1]);
+    }
+    // dK += Q^T dS of the last two tiles
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {
+      const int db = ch % DB, mm = ch / DB;
+      const bf16x8 ak = ch == 0 ? opk[0] : read_tr<D>(qbuf(bo), tr_off, db, mm);
+      dka[db] = mfma(ak, word8(sw[B], mm), dka[db]);
+    }
+#pragma unroll
+    for (int ch = 0; ch < DK; ++ch) {
+      const int db = ch % DB, mm = ch / DB;
+      dka[db] = mfma(read_tr<D>(qbuf(cur), tr_off, db, mm), word8(sw[B ^ 1], mm), dka[db]);
+    }
+  }
+
+  // all steps of one side, tiles t0 .. nQT - 1, then the tail; the P side's steps on
   // tiles [t0 + 4, tf) (causal; [0, tf) otherwise) skip the visibility test
   template <bool PSIDE>
   __device__ __forceinline__ void run(int t0, int nQT, int tf) {
-    const int tend = nQT + 2;
+    const int tend = nQT;
     int t = t0;
     auto six = [&](auto guard) {
       constexpr bool G = decltype(guard)::value;
@@ -802,6 +846,14 @@ struct DkDvPair {
         step_p<0, true>(t, (t - t0) % NB);
       else
         step_d<0>(t, (t - t0) % NB);
+      ++t;
+    }
+    // the last step was t - 1
+    const int last = (t - 1 - t0) % NB;
+    if ((t - 1 - t0) & 1) {
+      if constexpr (PSIDE) tail_p<1>(last); else tail_d<1>(last);
+    } else {
+      if constexpr (PSIDE) tail_p<0>(last); else tail_d<0>(last);
     }
   }
 };

@@ -18,22 +18,24 @@
 //              per lane), with K's and V's rows permuted so that dS^T comes
 //              out in the B-operand layout of dQ^T += K^T dS^T, K^T being read
 //              with the transposing LDS read;
-//   * dK, dV:  one workgroup per (128-key block, head), 4 wavefronts of 32
-//              keys, the block's K and V held in registers; query tiles (Q,
-//              dO, LSE, D) of 32 rows through LDS.  Here S = Q K^T keeps one
-//              key per lane, with Q's and dO's rows permuted, so P and dS come
-//              out as B operands of dV^T += dO^T P and dK^T += Q^T dS.
-// The dQ kernel, and the dK/dV kernel at d = 128, are software-pipelined: four
-// tile buffers, and each step interleaves the score MFMAs of the next tile, the
-// gradient MFMAs of the previous one and the vector work of the current one.  At
-// d = 64 the dK/dV kernel is the plain loop, which fits two wavefronts per SIMD:
-// tiles double-buffered, the next one loaded into registers while the current
-// one is used, then written to the other buffer before the step's single barrier.
+//   * dK, dV:  one workgroup per (128-key block, head), the block's K and V held
+//              in registers, 32 keys per wavefront; query tiles (Q, dO, LSE, D)
+//              of 32 rows through LDS.  Here S = Q K^T keeps one key per lane,
+//              with Q's and dO's rows permuted, so P and dS come out as B
+//              operands of dV^T += dO^T P and dK^T += Q^T dS.
+// The dQ kernel, and the dK/dV kernel at d = 128, are software-pipelined: each step
+// interleaves the score MFMAs of the next tile, the gradient MFMAs of an earlier one
+// and the vector work of the current one.  At d = 128 the dK/dV work of each 32
+// keys is split between two wavefronts on one SIMD (K, S, P, dV on one side; V, dP,
+// dS, dK on the other, P passed through LDS).  At d = 64 the dK/dV kernel is the
+// plain loop of 4 wavefronts, two per SIMD: tiles double-buffered, the next one
+// loaded into registers while the current one is used, then written to the other
+// buffer before the step's single barrier.
 //
 // A negative scale flips every sign bit of Q, a zero scale zeroes Q (the
 // kernels then use the positive multiplier |scale| * log2(e)): dQ = scale *
 // (dS K) and dK = |scale| * (dS^T Q') for the flipped Q', which are the
-// gradients of the original problem.  The pipelined dK/dV kernel instead takes Q
+// gradients of the original problem.  The d = 128 dK/dV kernel instead takes Q
 // unchanged with the signed multiplier scale * log2(e) and dK = scale * (dS^T Q),
 // the same products with the sign moved out of the operand.
 #include "fa_device.h"
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------- dQ
-// Software pipeline over key tiles, as in the dK/dV kernel: step t issues the MFMAs
+// Software pipeline over key tiles: step t issues the MFMAs
 // of S^T_{t+1} = K_{t+1} Q'^T and dP^T_{t+1} = V_{t+1} dO^T, the MFMAs of
 // dQ^T += K_{t-1}^T dS^T_{t-1}, and the vector work that turns S^T_t, dP^T_t into
 // dS^T_t.  Four K/V buffers hold tiles t-1 .. t+2.  To stay within two wavefronts
@@ -986,9 +988,8 @@ hipError_t launch_d(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v,
                      dout, a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
   const int nKB = (N + 127) / 128;
-  // d = 128: the pipelined kernel (one wavefront per SIMD either way); d = 64: the
-  // plain one, which fits two wavefronts per SIMD and hides its latencies with the
-  // second (the pipelined one would need more than the 256 registers that allows)
+  // d = 128: wavefront pairs, 8 wavefronts; d = 64: the plain loop, 4 wavefronts (the
+  // pairs at d = 64 were bit-identical but 11 % slower on B16 H16 N1024)
   if constexpr (D == 128)
     hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)(nKB * BH)), dim3(512), 0, a.stream, q, k,
                        v, dout, a.lse, a.delta, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), BH, N,

@@ -576,9 +576,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(
 // Eight wavefronts, two per SIMD.  Wavefront w < 4 (the P side) and wavefront w + 4 (the
 // dS side) share the 32 keys 32 w .. 32 w + 31 of the block.  The P side holds K and dV:
 // it computes S = Q K^T, turns S into P and accumulates dV^T += dO^T P.  The dS side holds
-// V and dK: it computes dP = dO V^T, takes P from the P side through LDS (in fp32, so dS is
-// formed from exactly the values the P side rounded for dV), forms dS = P (dP - D) and
-// accumulates dK^T += Q^T dS.  Each side keeps about half the state of one wavefront doing
+// V and dK: it computes dP = dO V^T, takes P from the P side through LDS in fp32 (the
+// values the P side rounds to bf16 for dV, so dS is what one wavefront doing both would
+// form), forms dS = P (dP - D) and accumulates dK^T += Q^T dS.  Each side keeps about half the state of one wavefront doing
 // both, so each fits the 256 registers that two wavefronts per SIMD allow, and every SIMD
 // runs one wavefront of each side, whose MFMAs and vector work overlap.  Step t:
 //   P side:  MFMAs of S_{t+1} = Q_{t+1} K^T and dV += dO_{t-1}^T P_{t-1}; vector work

@@ -149,6 +149,24 @@ def test_backward_full_size_heads(fa):
         assert all(torch.equal(x, y) for x, y in zip(got, again))
 
 
+def test_backward_d64_workload_heads(fa):
+    """The d = 64 workload (B16 H16 N1024 non-causal) in its launch configuration (the
+    plain dK/dV loop and the pipelined dQ kernel at d = 64), two whole heads checked."""
+    w = synthetic.workload("bf16_b16h16n1024d64")
+    G.log(f"case backward {w.name}")
+    q, k, v, _ = synthetic.workload_inputs(w)
+    do = synthetic.draw_qkv(w.B, w.H, w.N, w.d, seed=w.seed + 100, dtype="bf16")[0]
+    got, o = _grads(fa, q, k, v, do, w.causal, w.scale, with_o=True)
+    for b, h in ((0, 0), (15, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        ref = A.backward(q[sl], k[sl], v[sl], do[sl], w.causal, w.scale, o=o[sl])
+        e = _errors([x[sl] for x in got], ref)
+        G.log(f"  head ({b},{h}) normwise errors dQ {e[0]:.2e} dK {e[1]:.2e} dV {e[2]:.2e}")
+        assert max(e) <= TOL
+        assert max(_elem([x[sl] for x in got], ref, q[sl], k[sl], v[sl], do[sl], o[sl], w.causal, w.scale)) <= \
+            G.BWD_ELEM_TOL
+
+
 def test_backward_long_sequence_head(fa):
     """The long-sequence workload (B1 H32 N16384 d128 causal) in its launch configuration;
     one whole head against the fp64 gradient oracle (every N x N product materialised)."""

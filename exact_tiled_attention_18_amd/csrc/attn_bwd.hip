@@ -10,10 +10,12 @@
 // As in the forward pass, no N x N matrix is stored: P is recomputed tile by
 // tile from the scores and the saved LSE, P = exp(scale * q.k - LSE).
 //
-// Three kernels, no atomics (the result is bitwise reproducible):
-//   * delta:   D_i = rowsum(dO * O) in fp32 (one read of O and dO);
+// Two kernels, no atomics (the result is bitwise reproducible):
 //   * dQ:      one workgroup per (256-query block, head), 8 wavefronts of 32
-//              queries; K and V tiles of 32 keys through LDS.  As in the
+//              queries; K and V tiles of 32 keys through LDS.  Its prologue also
+//              forms D_i = rowsum(dO * O) in fp32 for its queries, from the dO
+//              row it loads anyway and one read of the O row, and writes D for
+//              the dK/dV kernel, which runs after it.  As in the
 //              forward kernel the scores are transposed (S^T = K Q^T, one query
 //              per lane), with K's and V's rows permuted so that dS^T comes
 //              out in the B-operand layout of dQ^T += K^T dS^T, K^T being read
@@ -160,34 +162,6 @@ __device__ __forceinline__ void store_rows(uint16_t* dst_row, const f32x16 (&acc
   for (int db = 0; db < D / 32; ++db) store_row_bf16(dst_row + db * 32, acc[db], mul, g);
 }
 
-// ---------------------------------------------------------------- D = rowsum(dO * O)
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o,
-                                                        const uint16_t* __restrict__ dout,
-                                                        float* __restrict__ delta, int64_t rows) {
-  constexpr int C = D / 4;  // columns per thread, four threads per row
-  const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
-  const int part = threadIdx.x & 3;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint16_t* po = o + row * D + part * C;
-    const uint16_t* pd = dout + row * D + part * C;
-#pragma unroll
-    for (int i = 0; i < C; i += 8) {
-      const uint4 a = *reinterpret_cast<const uint4*>(po + i), b = *reinterpret_cast<const uint4*>(pd + i);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = fmaf(bf16_lo(aw[j]), bf16_lo(bw[j]), acc);
-        acc = fmaf(bf16_hi(aw[j]), bf16_hi(bw[j]), acc);
-      }
-    }
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  if (row < rows && part == 0) delta[row] = acc;
-}
-
 // ---------------------------------------------------------------- dQ
 // Software pipeline over key tiles: step t issues the MFMAs
 // of S^T_{t+1} = K_{t+1} Q'^T and dP^T_{t+1} = V_{t+1} dO^T, the MFMAs of
@@ -311,9 +285,10 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
+                                                          const uint16_t* __restrict__ o,
                                                           const uint16_t* __restrict__ dout,
                                                           const float* __restrict__ lse,
-                                                          const float* __restrict__ delta,
+                                                          float* __restrict__ delta,
                                                           uint16_t* __restrict__ dq, int BH, int N, int nQB, float c,
                                                           float dq_mul, uint32_t qxor, uint32_t qand) {
   using W = DqPipe<D, CAUSAL>;
@@ -348,20 +323,31 @@ __global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __rest
   w.krow = row_reader<D>(permuted_row(w.li), w.g);
   w.tr_off = tr_reader<D>(lane);
 
-  // this lane's query: Q' fragments in registers, its dO row halves into LDS
+  // this lane's query: Q' fragments in registers, its dO row halves into LDS, and
+  // D = rowsum(dO * O) over the lane's half of the row (the columns of its Q and dO
+  // fragments) plus the partner lane's half
+  float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < DK; ++ks) {
-    uint4 a = make_uint4(0, 0, 0, 0), b = a;
+    uint4 a = make_uint4(0, 0, 0, 0), b = a, ov = a;
     if (w.qi < N) {
       a = *reinterpret_cast<const uint4*>(q + base + (size_t)w.qi * D + ks * 16 + w.g * 8);
       b = *reinterpret_cast<const uint4*>(dout + base + (size_t)w.qi * D + ks * 16 + w.g * 8);
+      ov = *reinterpret_cast<const uint4*>(o + base + (size_t)w.qi * D + ks * 16 + w.g * 8);
     }
     a = make_uint4((a.x ^ qxor) & qand, (a.y ^ qxor) & qand, (a.z ^ qxor) & qand, (a.w ^ qxor) & qand);
     w.qf[ks] = __builtin_bit_cast(bf16x8, a);
     *reinterpret_cast<uint4*>(dos + w.qloc * W::DS + ks * 32 + w.g * 16) = b;
+    const uint32_t ow[4] = {ov.x, ov.y, ov.z, ov.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dpart = fmaf(bf16_lo(ow[j]), bf16_lo(bw[j]), dpart);
+      dpart = fmaf(bf16_hi(ow[j]), bf16_hi(bw[j]), dpart);
+    }
   }
+  w.dd = sum_pair(dpart);  // 0 for rows past N
+  if (w.qi < N && w.g == 0) delta[(size_t)bh * N + w.qi] = w.dd;
   w.lse2 = w.qi < N ? lse[(size_t)bh * N + w.qi] * kLog2e : 0.f;
-  w.dd = w.qi < N ? delta[(size_t)bh * N + w.qi] : 0.f;
 #pragma unroll
   for (int db = 0; db < W::DB; ++db)
 #pragma unroll
@@ -973,19 +959,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(
 template <int D, bool CAUSAL>
 hipError_t launch_d(const BwdArgs& a) {
   const int BH = (int)(a.B * a.H), N = (int)a.N;
-  const int64_t rows = (int64_t)BH * N;
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* k = static_cast<const uint16_t*>(a.k);
   const uint16_t* v = static_cast<const uint16_t*>(a.v);
   const uint16_t* o = static_cast<const uint16_t*>(a.o);
   const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, a.stream, o, dout,
-                     a.delta, rows);
   const float c = a.scale == 0.f ? 1.f : fabsf(a.scale) * kLog2e;
   const uint32_t qxor = a.scale < 0.f ? 0x80008000u : 0u;
   const uint32_t qand = a.scale == 0.f ? 0u : 0xFFFFFFFFu;
   const int nQB = (N + 255) / 256;
-  hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v,
+  // dQ first: it writes D, which the dK/dV kernel reads
+  hipLaunchKernelGGL((bwd_dq_pipe_kernel<D, CAUSAL>), dim3((unsigned)(nQB * BH)), dim3(512), 0, a.stream, q, k, v, o,
                      dout, a.lse, a.delta, static_cast<uint16_t*>(a.dq), BH, N, nQB, c, a.scale, qxor, qand);
   const int nKB = (N + 127) / 128;
   // d = 128: wavefront pairs, 8 wavefronts; d = 64: the plain loop, 4 wavefronts (the

@@ -407,8 +407,12 @@ __global__ __launch_bounds__(512) void bwd_dq_pipe_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- dK, dV
+// two wavefronts per SIMD (stated, so that the compiler budgets 256 registers per
+// wavefront): it then keeps every accumulator in VGPRs and uses the VGPR forms of the
+// MFMAs.  Without the bound it put S, dP, dK and dV in accumulation registers and
+// copied them out and back, 96 of the step's 330 vector instructions.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int BH, int N, float c, float dk_mul, uint32_t qxor,

@@ -227,3 +227,35 @@ def backward(q, k, v, do, causal: bool, scale: float, o=None):
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def backward_sampled(q, k, v, do, o, lse, causal: bool, scale: float, rows, keys):
+    """Some rows of dQ and some keys' rows of dK and dV for one head (q, k, v, do, o:
+    [N, d]; lse: [N]), by the formulas of ``backward`` with the forward's output O and
+    logsumexp LSE taken as given: the backward operation receives both, and with them
+    P_ij = exp(scale q_i . k_j - LSE_i) and D_i = sum_c dO_ic O_ic need no pass over a
+    whole row of S.  Row i of dQ uses row i of P and dS, row j of dK and dV uses column
+    j, so each costs O(N d) and long sequences can be sampled.  Returns float64
+    (dQ[rows], dK[keys], dV[keys])."""
+    q, k, v, do, o, lse = (_as_f64(x) for x in (q, k, v, do, o, lse))
+    dd = (do * o).sum(axis=1)
+    rows, keys = np.asarray(rows), np.asarray(keys)
+    dq = np.zeros((len(rows), q.shape[1]))
+    for n, i in enumerate(rows):
+        s = scale * (k @ q[i])  # row i of S
+        if causal:
+            s[i + 1:] = -np.inf
+        p = np.exp(s - lse[i])
+        ds = p * (v @ do[i] - dd[i])  # dP_ij = dO_i . V_j
+        dq[n] = scale * (ds @ k)
+    dk = np.zeros((len(keys), k.shape[1]))
+    dv = np.zeros((len(keys), v.shape[1]))
+    for n, j in enumerate(keys):
+        s = scale * (q @ k[j])  # column j of S
+        if causal:
+            s[:j] = -np.inf
+        p = np.exp(s - lse)
+        ds = p * (do @ v[j] - dd)
+        dk[n] = scale * (ds @ q)
+        dv[n] = p @ do
+    return dq, dk, dv

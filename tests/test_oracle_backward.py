@@ -106,3 +106,18 @@ def test_given_output_moves_only_dq_dk_by_the_closed_form():
     assert np.abs((dq2 - dq1)[0, 0] - want_dq).max() < 1e-12
     assert np.abs((dk2 - dk1)[0, 0] - want_dk).max() < 1e-12
     assert np.abs(dv2 - dv1).max() == 0.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_and_keys_equal_the_full_backward(causal):
+    """backward_sampled with the exact output and LSE reproduces the rows of dQ and the
+    keys' rows of dK and dV of the full backward (D from the same given output)."""
+    q, k, v, do = _case(40, 8, b=1, h=1)
+    scale = 0.6
+    o, lse = A.reference(q, k, v, causal, scale)
+    dq, dk, dv = A.backward(q, k, v, do, causal, scale, o=o)
+    rows, keys = np.array([0, 1, 17, 39]), np.array([0, 5, 38, 39])
+    sq, sk, sv = A.backward_sampled(q[0, 0], k[0, 0], v[0, 0], do[0, 0], o[0, 0], lse[0, 0], causal, scale, rows, keys)
+    assert np.abs(sq - dq[0, 0, rows]).max() < 1e-12
+    assert np.abs(sk - dk[0, 0, keys]).max() < 1e-12
+    assert np.abs(sv - dv[0, 0, keys]).max() < 1e-12

@@ -247,6 +247,53 @@ def test_fp8_scales(fa, scale, p_bf16):
     assert rel <= (G.FP8_PBF16_O_TOL if p_bf16 else G.FP8_O_TOL) and el <= G.FP8_LSE_TOL
 
 
+def _steady_shift_moves(q8, k8, qs, ks, causal, scale):
+    """How many times the lazy shift (moved to a 64-key tile's row maximum when that
+    exceeds it by more than 2, in log2 units) moves in the unmasked steps after a row
+    block's first tile, replayed in fp64 on the dequantised codes of head (0, 0).  A
+    256-query block's unmasked tiles are those wholly before its first query."""
+    qd = F.dequantize(q8.cpu().numpy(), qs.cpu().numpy())[0, 0]
+    kd = F.dequantize(k8.cpu().numpy(), ks.cpu().numpy())[0, 0]
+    n = qd.shape[0]
+    s = (qd @ kd.T) * scale * np.log2(np.e)
+    moves = 0
+    for i in range(n):
+        q0 = i // 256 * 256
+        n_full = (min(n, q0 + 1) if causal else n) // 64
+        m = -np.inf
+        for t in range((n + 63) // 64):
+            hi = min(n, 64 * t + 64, i + 1 if causal else n)
+            if 64 * t >= hi:
+                break
+            mt = s[i, 64 * t:hi].max()
+            if mt > m + 2.0:
+                m = mt
+                moves += int(1 <= t < n_full)
+    return moves
+
+
+@pytest.mark.parametrize("p_bf16", [False, True])
+def test_fp8_rising_maxima(fa, p_bf16):
+    """K rows scaled by 1 + 6 j / N, so the row maxima keep rising along the keys: the lazy
+    shift moves in unmasked steps (counted on the dequantised codes), and O and the rounded
+    row sum are carried to the new shift.  G5b on every output of both heads."""
+    B, H, N, d = 1, 2, 1100, 128
+    G.log(f"case fp8 rising maxima p_bf16={p_bf16}")
+    q, k, v = synthetic.draw_qkv(B, H, N, d, seed=651, dtype="bf16")
+    ramp = 1.0 + 6.0 * torch.arange(N, dtype=torch.float32) / N
+    k = (k.float() * ramp[None, None, :, None]).to(torch.bfloat16)
+    signs = synthetic.draw_signs(d, 652)
+    for causal in (False, True):
+        for scale in (d ** -0.5, 0.5):
+            o, lse, (q8, k8, v8t, qs, ks, vs) = _fp8_case(fa, q, k, v, signs, causal, scale, p_bf16=p_bf16)
+            moves = _steady_shift_moves(q8, k8, qs, ks, causal, scale)
+            rel, ab, el = G.fp8_errors(o, lse, q8, k8, v8t, qs, ks, vs, causal, scale, heads=[(0, 0), (0, 1)])
+            G.log(f"  causal={causal} scale={scale:.4f}: {moves} shift moves in unmasked steps of head 0; "
+                  f"scaled err {rel:.3e} (abs {ab:.3e})  LSE rel {el:.3e}")
+            assert moves > 100
+            assert rel <= (G.FP8_PBF16_O_TOL if p_bf16 else G.FP8_O_TOL) and el <= G.FP8_LSE_TOL
+
+
 def test_fp8_workload_full_size(fa):
     """The fp8 workload (B2 H16 N8192, x50 outliers) in the bench's launch configuration.
     G5a on three whole heads; G5b on two whole heads (all 8192 rows) and sampled rows of a

@@ -122,6 +122,7 @@ struct Attn8 {
   float m, l, lh, alpha, msub, rs;
   float cst, inv_frac;  // softmax multiplier and 1 / f of the tile being softmaxed
   int psc;               // its E8M0 scale 127 + e + 1
+  float lfac;            // and log2 f
   float ks_n, vs_n;      // raw K and V tile scales of the next tile (loaded one step ahead)
   float msub_q;
 
@@ -199,13 +200,18 @@ struct Attn8 {
   __device__ __forceinline__ float max2(float a, float b) const { return __builtin_amdgcn_fmed3f(a, b, pinf); }
   __device__ __forceinline__ void softmax_slice(int ch, int B, int t, bool guard) {
     if (ch == 0) {
-      // this tile's factors: multiplier, r = sv / svmax = 2^(e+1) f, 1 / f, E8M0 scale
-      cst = uniform(cq * ks_n);
-      const float lr = log2_fast(vs_n) - log2_svmax;        // log2 r <= 0
-      const float e = fmaxf(__builtin_floorf(lr), -120.f);  // E8M0 stays in range
-      const float lf = uniform(lr - e - 1.f);               // log2 f, in [-1, 0) unless clamped
-      inv_frac = uniform(exp2_fast(-lf));
-      psc = __builtin_amdgcn_readfirstlane(128 + (int)e);
+      // this tile's factors: multiplier, r = sv / svmax = 2^(e+1) f, 1 / f, E8M0 scale.
+      // A 128-row quantisation tile holds key tiles 2u and 2u + 1, so the odd steps (B
+      // = 1) keep the factors of the step before
+      if (B == 0) {
+        cst = uniform(cq * ks_n);
+        const float lr = log2_fast(vs_n) - log2_svmax;        // log2 r <= 0
+        const float e = fmaxf(__builtin_floorf(lr), -120.f);  // E8M0 stays in range
+        lfac = uniform(lr - e - 1.f);                         // log2 f, in [-1, 0) unless clamped
+        inv_frac = uniform(exp2_fast(-lfac));
+        psc = __builtin_amdgcn_readfirstlane(128 + (int)e);
+      }
+      const float lf = lfac;
       if (guard) mask_scores(B, t);
       const f32x16& s0 = sbuf[B][0];
       const f32x16& s1 = sbuf[B][1];
@@ -286,7 +292,7 @@ struct Attn8 {
         store_k(sk_w, stg_k);
       }
       if (ch == 2) {
-        load_scales(t + 1);
+        if (B == 1) load_scales(t + 1);  // an even tile next: a new quantisation tile
         stg_k = load_k(t + 4);
         stg_v = load_v(t + 2);
       }

@@ -228,11 +228,13 @@ struct Attn8 {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       const float mt = cst * max2(__uint_as_float(sw[0]), __uint_as_float(sw[1]));  // -inf when no key is visible
       const float m_new = mt > m + kSlack ? mt : m;
-      alpha = m_new == -kInf ? 1.f : exp2_fast(m - m_new);
+      // unmasked steps come after step 0, in which every row sees key 0: the shift is
+      // finite there and needs no test for an empty row
+      alpha = guard && m_new == -kInf ? 1.f : exp2_fast(m - m_new);
       m = m_new;
       l *= alpha;
       // 2^(cst*s - m + 6 + log2 f): the scaled probability that enters e4m3
-      msub_q = m_new == -kInf ? 0.f : m_new - kPShift - lf;
+      msub_q = guard && m_new == -kInf ? 0.f : m_new - kPShift - lf;
       rs = 0.f;
     } else if (ch == 1 || ch == 2) {
       f32x16& s = sbuf[B][ch - 1];

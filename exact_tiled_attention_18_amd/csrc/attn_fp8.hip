@@ -82,7 +82,10 @@ static_assert(kBc * kD / 16 == kThreads && kD * kBc / 16 == kThreads, "one 16-by
 __device__ __forceinline__ int permuted_row(int i) { return i ^ ((((i >> 2) ^ (i >> 3)) & 1) * 0xC); }
 
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the conversion writes one half of its destination and keeps the other; the second
+  // one overwrites the kept half, so the first may keep any bits -- a's own, which
+  // spares zeroing a register for it
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (uint32_t)w;
 }

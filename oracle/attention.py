@@ -235,8 +235,9 @@ def backward_sampled(q, k, v, do, o, lse, causal: bool, scale: float, rows, keys
     logsumexp LSE taken as given: the backward operation receives both, and with them
     P_ij = exp(scale q_i . k_j - LSE_i) and D_i = sum_c dO_ic O_ic need no pass over a
     whole row of S.  Row i of dQ uses row i of P and dS, row j of dK and dV uses column
-    j, so each costs O(N d) and long sequences can be sampled.  Returns float64
-    (dQ[rows], dK[keys], dV[keys])."""
+    j, so each costs O(N d) and long sequences can be sampled.  The gradients are
+    those the pages' training use needs (FlashAttention-2 wiki page, "Leistung und
+    Effizienz"), as in ``backward``.  Returns float64 (dQ[rows], dK[keys], dV[keys])."""
     q, k, v, do, o, lse = (_as_f64(x) for x in (q, k, v, do, o, lse))
     dd = (do * o).sum(axis=1)
     rows, keys = np.asarray(rows), np.asarray(keys)
